@@ -1,0 +1,239 @@
+"""Benchmark of the HSA hot path on one MI355X.
+
+One step = one chunk of one layer through the whole path: the CAG schedule and block
+budget on the host, then pool Q, pool K (block + frame means), frame top-k, block top-k
+and block-sparse attention on the GPU, each a C-ABI call on torch's current stream.
+Default workload: the 480p layer at chunk 7 of 7 (12 heads x 128, 4680 query tokens
+against 21 frames = 32760 key tokens, 64-token blocks, 8 frames x 8 blocks per row).
+
+Steps cycle over R independent layers' inputs (each ~230 MB of Q/K/V, R*230 MB well
+above the 256 MB Infinity Cache), so every step streams its K/V from HBM as in a real
+layer-by-layer rollout. Inputs are resident in HBM before timing starts.
+
+Printed: one JSON line with the headline (dense-equivalent HSA TFLOP/s), per-kernel
+times from HIP events recorded on the launch stream, the attention kernel's roofline
+(algorithmic FLOPs per launch / mean duration vs the 2.5 PFLOP/s bf16 dense peak), the
+selection overhead and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import sparse_attention_autoregressive_amd as lf  # noqa: E402
+from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, Workspace, attend, pool_k,  # noqa: E402
+                                                          pool_q, select_blocks, select_frames)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "HSA effective TFLOP/s (dense-equiv) + % MFMA peak + select overhead %, 480p"
+KERNELS = ["pool_q", "pool_k", "select_frames", "select_blocks", "attn"]
+
+
+def chunk_flops(w):
+    fpc = len(w.current)
+    return [float(fpc * w.tpf * fpc * i * w.tpf) for i in range(1, w.n_chunks + 1)]
+
+
+def block_lens(w):
+    nb = -(-w.tpf // w.bs)
+    return np.array([min(w.bs, w.tpf - j * w.bs) for j in range(nb)], dtype=np.int64)
+
+
+def flops_of(w, blocks: np.ndarray):
+    """(dense-equivalent, active) attention FLOPs of one chunk, 4*d per query-key pair
+    (Q K^T and P V, 2 FLOPs per multiply-add each), with true ragged block lengths."""
+    lens = block_lens(w)
+    nb = len(lens)
+    n_qb = blocks.shape[2]
+    qlen = lens[np.arange(n_qb) % nb]
+    dense = 4.0 * w.d * w.B * w.H * float(qlen.sum()) * w.lk
+    active = 4.0 * w.d * float((qlen[None, None, :] * lens[blocks % nb].sum(axis=-1)).sum())
+    return dense, active
+
+
+def pool_bytes(w, n_frames, with_frames):
+    """Algorithmic HBM bytes of one lf_pool call: read every token once, write the means."""
+    esz = 2 if w.dtype == "bf16" else 4
+    nb = -(-w.tpf // w.bs)
+    rd = w.B * w.H * n_frames * w.tpf * w.d * esz
+    wr = w.B * w.H * n_frames * nb * w.d * 4 + (w.B * w.H * n_frames * w.d * 4 if with_frames else 0)
+    return rd + wr
+
+
+def run_cpu_baseline(w, heads: int):
+    """The CPU oracle (numpy fp64) on the first `heads` heads of one layer: pool, select
+    and attend. Returns (dense-equiv TFLOP/s, seconds, dense flops of the sample)."""
+    import dataclasses
+
+    import oracle
+    ws = dataclasses.replace(w, H=heads)
+    x = synth.make(ws)
+    q64, k64, v64 = x.np64()
+    k_b = w.k_b
+    t0 = time.perf_counter()
+    out = oracle.hsa(q64, k64, v64, tpf=ws.tpf, bs=ws.bs, n_kframes=ws.n_kframes, mem=ws.mem,
+                     forced=ws.forced, k_f=ws.k_f, k_b=k_b, scale=ws.scale)
+    dt = time.perf_counter() - t0
+    dense, _ = flops_of(ws, out["blocks"])
+    return dense / dt / 1e12, dt, dense
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="480p_chunk7of7", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--layers", type=int, default=4, help="independent input sets cycled per step")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU-oracle sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build targets one GPU; the HSA path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda")
+    w = synth.WORKLOADS[args.workload]
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    nb = lf.n_bpf(g)
+    dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    # a0 on the host: CAG schedule and block budget
+    s_sched, beta = lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
+    W_f = len(w.forced) + min(w.k_f, len(w.mem))
+    k_b = w.k_b if w.k_b is not None else lf.lf_block_budget(s_sched[w.chunk_index - 1],
+                                                             w.n_kframes * nb, W_f, nb)
+    plan = ChunkPlan(g, w.n_qframes, w.n_kframes, list(w.mem), list(w.forced), w.k_f, k_b, w.scale)
+
+    # inputs: layer 0 from the seeded host generator, the others drawn on the device
+    print(f"[bench] generating {args.layers} input sets for {w.name}", file=sys.stderr, flush=True)
+    x = synth.make(w)
+    sets = [(x.q.to(dev), x.k.to(dev), x.v.to(dev))]
+    pools = [w.q_pool if w.q_pool is not None else x.planted]
+    for li in range(1, args.layers):
+        sets.append(synth.make_on_device(w.B, w.H, w.n_qframes, w.n_kframes, w.tpf, w.bs, w.d, w.dtype,
+                                         w.seed + 100 * li, dev, pools))
+    wss = [Workspace(plan, dtype, dev) for _ in sets]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
+        ws = wss[i % len(sets)]
+        q, k, v = sets[i % len(sets)]
+        calls = [lambda: pool_q(ws, q), lambda: pool_k(ws, k), lambda: select_frames(ws),
+                 lambda: select_blocks(ws), lambda: attend(ws, q, k, v)]
+        for j, c in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            c()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(KERNELS))]
+                    for i in range(args.steps)]) * 1e3                      # us
+    mean_us = per.mean(axis=0)
+    med_us = np.median(per, axis=0)
+    ms_per_step = wall * 1e3 / args.steps
+
+    blocks = wss[0].blocks.cpu().numpy()
+    f_dense, f_active = flops_of(w, blocks)
+    t_attn = mean_us[4] * 1e-6
+    t_path = mean_us.sum() * 1e-6
+    attn_tflops = f_active / t_attn / 1e12
+    value = f_dense / (ms_per_step * 1e-3) / 1e12
+    sel_pct = 100.0 * (mean_us[2] + mean_us[3]) / mean_us[4]
+    pool_gbs = {
+        "pool_q": pool_bytes(w, w.n_qframes, False) / (mean_us[0] * 1e-6) / 1e9,
+        "pool_k": pool_bytes(w, w.n_kframes, True) / (mean_us[1] * 1e-6) / 1e9,
+    }
+    n_rows = w.B * w.H * plan.n_qb
+    sel_bytes = {
+        # q~ rows + the memory set's frame means per row + list writes
+        "select_frames": n_rows * (w.d * 4 + len(w.mem) * w.d * 4 + plan.W_f * 4),
+        # frames lists read, q~ per listed frame, each head's k~ once, list writes
+        "select_blocks": n_rows * (plan.W_f * 4 + plan.W_f * w.d * 4 + plan.W_b * 4)
+        + w.B * w.H * w.n_kframes * nb * w.d * 4,
+    }
+    sel_gbs = {k: sel_bytes[k] / (mean_us[2 + i] * 1e-6) / 1e9 for i, k in enumerate(sel_bytes)}
+
+    cpu = None
+    if args.cpu_heads > 0:
+        print(f"[bench] CPU oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
+        cpu_tflops, cpu_s, cpu_dense = run_cpu_baseline(w, args.cpu_heads)
+        cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{w.name}, heads 0..{args.cpu_heads - 1} of {w.H}: pool + select + attention "
+                         f"in numpy fp64 ({cpu_dense:.3e} dense-equiv FLOP in {cpu_s:.1f} s)",
+               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or platform.machine()}
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded planted-relevance Q/K/V; no model weights)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "tokens_per_frame": w.tpf,
+                   "block_size": w.bs, "query_tokens": w.lq, "key_tokens": w.lk, "W_f": plan.W_f,
+                   "W_b": plan.W_b, "k_f": w.k_f, "k_b": k_b, "cag_s_i": s_sched[w.chunk_index - 1],
+                   "cag_beta": beta, "input_sets": len(sets)},
+        "mfma_pct_peak_active": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
+        "select_overhead_pct": sel_pct,
+        "pool_select_pct_of_attn": 100.0 * (mean_us[:4].sum()) / mean_us[4],
+        "dense_equiv_tflops_attn_only": f_dense / t_attn / 1e12,
+        "dense_equiv_tflops_kernel_sum": f_dense / t_path / 1e12,
+        "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
+        "kernel_us_mean": dict(zip(KERNELS, [round(float(x), 2) for x in mean_us])),
+        "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in med_us])),
+        "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
+        "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
+                     "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

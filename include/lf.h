@@ -1,0 +1,170 @@
+/*
+ * lf.h -- C ABI of the MI355X (gfx950) implementation of Light Forcing's Hierarchical
+ * Sparse Attention (HSA) and Chunk-Aware Growth (CAG) schedule, for one chunk of an
+ * autoregressive video-diffusion transformer.
+ *
+ * Citations name the page and its part:
+ *   [S1]/[S2]/[S3]  Light Forcing summary (paper.rainbus.top/paper/2602.04789), the
+ *                   execution-flow paragraph, stage 1 (CAG), stage 2 (token
+ *                   compression), stage 3 (two-level mask selection + block-sparse
+ *                   attention).
+ *   [G2.1]/[G2.2]   Light Forcing technical summary (gist.science/paper/2602.04789),
+ *                   section 2.1 (CAG) and section 2.2 (HSA).
+ *
+ * Conventions shared by every call
+ *   - Return value: lf_status; LF_OK (0) on success. On failure nothing is enqueued,
+ *     no output is written, and lf_last_error() returns a message for this thread.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t, e.g. the value of
+ *     torch.cuda.current_stream().cuda_stream; NULL means the default stream). All
+ *     tensors are caller-owned device buffers, row-major and contiguous, 16-byte
+ *     aligned, and must stay alive until the stream work completes. The library
+ *     allocates nothing, keeps no pointer after returning, and fully overwrites each
+ *     output. No atomics are used: identical inputs give bitwise-identical outputs.
+ *   - Precondition (not checked on the device): input values are finite.
+ *   - Token geometry (frame-aligned blocks): frame f holds tokens [f*tpf, (f+1)*tpf);
+ *     block j of a frame holds its tokens [j*bs, min((j+1)*bs, tpf)), so each frame has
+ *     n_bpf = ceil(tpf/bs) blocks, the last one possibly shorter; the global block id of
+ *     block j of frame f is f*n_bpf + j. Queries use the same rule on the chunk's own
+ *     frames (query block r = frame r/n_bpf, block r%n_bpf).
+ *   - Tensors are [B, H, tokens, d]: batch, head, token, channel.
+ */
+#ifndef LF_H
+#define LF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LF_ABI_VERSION 1
+
+typedef enum {
+  LF_OK = 0,
+  LF_ERR_INVALID_ARG = 1, /* a pointer, size, id or set violates the contract       */
+  LF_ERR_UNSUPPORTED = 2, /* valid in principle, but not built for (dtype, d, sizes) */
+  LF_ERR_INFEASIBLE = 3,  /* CAG target cannot be met without clamping               */
+  LF_ERR_HIP = 4          /* the HIP runtime reported an error at launch             */
+} lf_status;
+
+typedef enum { LF_FP32 = 0, LF_BF16 = 1 } lf_dtype;
+
+/* B batch, H heads, d head dim, tokens_per_frame (tpf), block_size (bs). */
+typedef struct {
+  int32_t B, H, d, tokens_per_frame, block_size;
+} lf_geom;
+
+/* Message for the last failing call on the calling thread ("" if none). The pointer
+ * stays valid until the next lf_* call on this thread. */
+const char* lf_last_error(void);
+
+/* LF_ABI_VERSION of the loaded library. */
+int32_t lf_abi_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * lf_cag_schedule -- [S1], [G2.1]: per-chunk sparsity s_1..s_n of Chunk-Aware Growth.
+ * Host only, synchronous, no GPU needed.
+ *   s_1 = 0 (the first chunk keeps dense attention); s_i = s_base - alpha_i * beta for
+ *   i > 1, with beta chosen so that the attention FLOPs kept over all chunks,
+ *   sum_i F_i (1 - s_i), equal (1 - s_target) * sum_i F_i.
+ * n_chunks >= 2; T >= 1 denoising steps; 0 <= s_target < 1; 0 < s_base < 1.
+ * chunk_flops[i] (host, n_chunks entries, > 0): dense attention FLOPs of chunk i+1 in
+ *   any common unit (for equal chunks against a growing cache, F_i is proportional to i).
+ * alpha (host, n_chunks entries, or NULL): the alpha_i weights. NULL selects
+ *   alpha_i = 1/sqrt(i*T), this library's reading of "alpha_i proportional to 1/sqrt(T),
+ *   the noise level reached by chunk i". alpha_1 is ignored.
+ * Outputs (host): s_out[n_chunks], *beta_out.
+ * Errors: LF_ERR_INVALID_ARG for bad sizes/pointers/values; LF_ERR_INFEASIBLE when the
+ *   solution has beta < 0 or some s_i outside [0, 1) (nothing is clamped).
+ * ------------------------------------------------------------------------------- */
+lf_status lf_cag_schedule(int32_t n_chunks, int32_t T, double s_base, double s_target,
+                          const double* chunk_flops, const double* alpha, double* s_out,
+                          double* beta_out);
+
+/* ---------------------------------------------------------------------------------
+ * lf_block_budget -- turns a chunk sparsity s into the per-frame block top-k k_b.
+ * The pages leave this step to a hyper-parameter table that is not available; this
+ * library keeps round-half-up((1 - s) * n_kblocks / W_f) blocks per selected frame,
+ * clamped to [1, n_bpf], so the W_f selected frames hold about (1 - s) of the
+ * n_kblocks key blocks. Host only, synchronous.
+ * Errors: LF_ERR_INVALID_ARG if s is not in [0, 1], n_kblocks < 1, W_f < 1, n_bpf < 1
+ *   or k_b_out is NULL.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_block_budget(double s, int32_t n_kblocks, int32_t W_f, int32_t n_bpf,
+                          int32_t* k_b_out);
+
+/* ---------------------------------------------------------------------------------
+ * lf_pool -- [S2] token compression by mean pooling.
+ * x: [B, H, n_frames*tpf, d] in dtype dt (LF_BF16 or LF_FP32).
+ * blk_out: [B, H, n_frames*n_bpf, d] fp32, the mean of each block's tokens (q~ for the
+ *   chunk's queries, k~ for keys), divided by the block's true token count.
+ * frm_out: [B, H, n_frames, d] fp32, the mean of each frame's tpf tokens (k^), or NULL
+ *   to skip (e.g. when pooling queries). Frame means are formed from the fp32 block
+ *   means weighted by their token counts.
+ * Limits: d in {64, 128}; 1 <= bs <= tpf; tpf <= 65536; n_frames >= 1; B, H >= 1.
+ * Errors: LF_ERR_INVALID_ARG (NULL/unaligned pointers, bad sizes), LF_ERR_UNSUPPORTED
+ *   (d or dtype), LF_ERR_HIP (launch).
+ * ------------------------------------------------------------------------------- */
+lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float* blk_out,
+                  float* frm_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * lf_select_frames -- [S3] frame stage: for every row (b, h, query block r), the frame
+ * relevance p_r(f) = <q~_r, k^_f> over the memory set M; the top-min(k_f, |M|)
+ * frames of M ranked by (score descending, frame id ascending) join the always-kept
+ * frames (sink, recent and current-chunk frames, passed as `forced`) to form T_r.
+ * q_blk: [B, H, n_qb, d] fp32 (lf_pool of the queries). k_frm: [B, H, n_kframes, d]
+ *   fp32 (frame means of all key frames; only those in M are read).
+ * mem, forced: HOST arrays of frame ids (n_mem, n_forced entries), each id in
+ *   [0, n_kframes), no duplicates, the two sets disjoint; n_forced + n_mem >= 1.
+ * frames_out: [B, H, n_qb, W_f] int32, W_f = n_forced + min(k_f, n_mem), each row
+ *   ascending.
+ * Limits: d in {64, 128}; n_kframes <= 256; k_f >= 0.
+ * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED (d, n_kframes), LF_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
+                           int32_t n_kframes, const int32_t* mem, int32_t n_mem,
+                           const int32_t* forced, int32_t n_forced, int32_t k_f,
+                           int32_t* frames_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * lf_select_blocks -- [S3] block stage: for every row and every tau in T_r, the block
+ * relevance o_r(tau, j) = <q~_r, k~_j^(tau)> over the frame's n_bpf blocks; the top
+ * min(k_b, n_bpf) blocks J_r(tau) ranked by (score descending, j ascending). The mask
+ * B_r(tau, j) = 1[tau in T_r, j in J_r(tau)] is emitted as an ascending list of global
+ * block ids tau*n_bpf + j.
+ * q_blk: [B, H, n_qb, d] fp32. k_blk: [B, H, n_kframes*n_bpf, d] fp32.
+ * frames: [B, H, n_qb, W_f] int32 device array, each row ascending and unique with ids
+ *   in [0, n_kframes) (the output of lf_select_frames). Ids out of range are skipped
+ *   (their list slots are left holding -1) rather than read.
+ * blocks_out: [B, H, n_qb, W_f*min(k_b, n_bpf)] int32.
+ * Limits: d in {64, 128}; n_bpf <= 64; n_kframes <= 65535; k_b >= 1; W_f >= 1.
+ * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, int32_t n_qb,
+                           int32_t n_kframes, const int32_t* frames, int32_t W_f, int32_t k_b,
+                           int32_t* blocks_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * lf_sparse_attn -- [S3], [G2.2] block-sparse attention: each query token t of query
+ * block r attends only to the tokens of the blocks listed for r,
+ *   o_t = sum_u softmax_u(scale * <q_t, k_u>) v_u   (softmax over the listed tokens).
+ * With every block listed this is dense attention (CAG's first chunk).
+ * q, o: [B, H, n_qframes*tpf, d]; k, v: [B, H, n_kframes*tpf, d]; all in dtype dt.
+ * blocks: [B, H, n_qb, W_b] int32 device array, n_qb = n_qframes*n_bpf; ids should be
+ *   unique (a repeated id is counted twice); ids outside [0, n_kframes*n_bpf) are
+ *   skipped. A row with no valid id produces zeros.
+ * LF_BF16 runs on bf16 matrix cores (fp32 accumulate and softmax) and needs d = 128 or
+ *   64 and bs <= 64; LF_FP32 runs in fp32 on the vector units and needs d in {64, 128}
+ *   and bs <= 128.
+ * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, lf_dtype dt,
+                         lf_geom g, int32_t n_qframes, int32_t n_kframes,
+                         const int32_t* blocks, int32_t W_b, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_H */

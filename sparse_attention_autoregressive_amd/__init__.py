@@ -1,0 +1,192 @@
+"""Light Forcing Hierarchical Sparse Attention (HSA) + Chunk-Aware Growth on MI355X.
+
+Thin Python binding of the C ABI in include/lf.h (liblf.so, built by
+`python -m sparse_attention_autoregressive_amd._build`). The functions carry the C
+names and only marshal arguments: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels. There is
+no fallback: if the library is missing, importing a function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = ["Geom", "LfError", "lf_abi_version", "lf_cag_schedule", "lf_block_budget",
+           "lf_pool", "lf_select_frames", "lf_select_blocks", "lf_sparse_attn", "library_path",
+           "n_bpf"]
+
+LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_INFEASIBLE, LF_ERR_HIP = range(5)
+LF_FP32, LF_BF16 = 0, 1
+_STATUS = {1: "LF_ERR_INVALID_ARG", 2: "LF_ERR_UNSUPPORTED", 3: "LF_ERR_INFEASIBLE", 4: "LF_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "liblf.so")
+
+
+class Geom(ctypes.Structure):
+    """lf_geom: batch, heads, head dim, tokens per frame, tokens per block."""
+
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("tokens_per_frame", ctypes.c_int32), ("block_size", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"Geom(B={self.B}, H={self.H}, d={self.d}, tpf={self.tokens_per_frame}, "
+                f"bs={self.block_size})")
+
+
+def n_bpf(g: Geom) -> int:
+    return -(-g.tokens_per_frame // g.block_size)
+
+
+class LfError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m sparse_attention_autoregressive_amd._build`")
+    lib = ctypes.CDLL(path)
+    i32, f64, f32, vp = ctypes.c_int32, ctypes.c_double, ctypes.c_float, ctypes.c_void_p
+    pf64 = ctypes.POINTER(ctypes.c_double)
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.lf_last_error.restype = ctypes.c_char_p
+    lib.lf_last_error.argtypes = []
+    lib.lf_abi_version.restype = i32
+    lib.lf_abi_version.argtypes = []
+    sig = {
+        "lf_cag_schedule": [i32, i32, f64, f64, pf64, pf64, pf64, pf64],
+        "lf_block_budget": [f64, i32, i32, i32, pi32],
+        "lf_pool": [vp, i32, Geom, i32, vp, vp, vp],
+        "lf_select_frames": [vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, vp, vp],
+        "lf_select_blocks": [vp, vp, Geom, i32, i32, vp, i32, i32, vp, vp],
+        "lf_sparse_attn": [vp, vp, vp, vp, i32, Geom, i32, i32, vp, i32, f32, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != LF_OK:
+        raise LfError(status, _load().lf_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> Optional[int]:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LF_BF16
+    if t.dtype == torch.float32:
+        return LF_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _i32_array(xs: Sequence[int]):
+    arr = (ctypes.c_int32 * max(1, len(xs)))(*[int(x) for x in xs])
+    return arr
+
+
+def lf_abi_version() -> int:
+    return int(_load().lf_abi_version())
+
+
+def lf_cag_schedule(n_chunks: int, T: int, s_base: float, s_target: float,
+                    chunk_flops: Sequence[float], alpha: Optional[Sequence[float]] = None):
+    """Host call: returns (s[0..n-1], beta)."""
+    lib = _load()
+    F = (ctypes.c_double * n_chunks)(*[float(x) for x in chunk_flops])
+    A = None if alpha is None else (ctypes.c_double * n_chunks)(*[float(x) for x in alpha])
+    s = (ctypes.c_double * n_chunks)()
+    beta = ctypes.c_double()
+    _check(lib.lf_cag_schedule(n_chunks, T, s_base, s_target, F, A, s, ctypes.byref(beta)))
+    return list(s), beta.value
+
+
+def lf_block_budget(s: float, n_kblocks: int, W_f: int, n_bpf_: int) -> int:
+    out = ctypes.c_int32()
+    _check(_load().lf_block_budget(s, n_kblocks, W_f, n_bpf_, ctypes.byref(out)))
+    return out.value
+
+
+def lf_pool(x: torch.Tensor, g: Geom, n_frames: int, blk_out: Optional[torch.Tensor] = None,
+            frm_out: Optional[torch.Tensor] = None, with_frames: bool = True):
+    """Block means [B,H,n_frames*n_bpf,d] fp32 and (optionally) frame means [B,H,n_frames,d]."""
+    lib = _load()
+    nb = n_bpf(g)
+    if blk_out is None:
+        blk_out = torch.empty((g.B, g.H, n_frames * nb, g.d), dtype=torch.float32, device=x.device)
+    if frm_out is None and with_frames:
+        frm_out = torch.empty((g.B, g.H, n_frames, g.d), dtype=torch.float32, device=x.device)
+    _check(lib.lf_pool(_dev(x, "x"), _dtype_code(x), g, n_frames, _dev(blk_out, "blk_out"),
+                       None if frm_out is None else _dev(frm_out, "frm_out"), _stream(x)))
+    return blk_out, frm_out
+
+
+def lf_select_frames(q_blk: torch.Tensor, k_frm: torch.Tensor, g: Geom, n_qb: int, n_kframes: int,
+                     mem: Sequence[int], forced: Sequence[int], k_f: int,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """T_r per row: [B,H,n_qb,W_f] int32, W_f = len(forced) + min(k_f, len(mem))."""
+    lib = _load()
+    W_f = len(forced) + min(k_f, len(mem))
+    if out is None:
+        out = torch.empty((g.B, g.H, n_qb, max(W_f, 1)), dtype=torch.int32, device=q_blk.device)
+    _check(lib.lf_select_frames(_dev(q_blk, "q_blk"), _dev(k_frm, "k_frm"), g, n_qb, n_kframes,
+                                _i32_array(mem), len(mem), _i32_array(forced), len(forced), k_f,
+                                _dev(out, "out"), _stream(q_blk)))
+    return out
+
+
+def lf_select_blocks(q_blk: torch.Tensor, k_blk: torch.Tensor, g: Geom, n_qb: int, n_kframes: int,
+                     frames: torch.Tensor, k_b: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mask B_r as ascending block-id lists: [B,H,n_qb,W_f*min(k_b,n_bpf)] int32."""
+    lib = _load()
+    W_f = frames.shape[-1]
+    W_b = W_f * min(k_b, n_bpf(g))
+    if out is None:
+        out = torch.empty((g.B, g.H, n_qb, W_b), dtype=torch.int32, device=q_blk.device)
+    _check(lib.lf_select_blocks(_dev(q_blk, "q_blk"), _dev(k_blk, "k_blk"), g, n_qb, n_kframes,
+                                _dev(frames, "frames"), W_f, k_b, _dev(out, "out"), _stream(q_blk)))
+    return out
+
+
+def lf_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geom, n_qframes: int,
+                   n_kframes: int, blocks: torch.Tensor, scale: float,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-sparse attention output [B,H,n_qframes*tpf,d] in q's dtype."""
+    lib = _load()
+    if out is None:
+        out = torch.empty_like(q)
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise TypeError("q, k, v and out must share a dtype")
+    _check(lib.lf_sparse_attn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                              _dtype_code(q), g, n_qframes, n_kframes, _dev(blocks, "blocks"),
+                              blocks.shape[-1], float(scale), _stream(q)))
+    return out

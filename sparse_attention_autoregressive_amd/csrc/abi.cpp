@@ -1,0 +1,240 @@
+// C ABI of the HSA library: argument validation on the host, the Chunk-Aware Growth
+// schedule (host math), and kernel launches on the caller's stream.
+// Every check happens before anything is enqueued; a failing call stores a message in
+// a thread-local buffer and returns a status. No exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/lf.h"
+#include "lf_kernels.h"
+
+namespace {
+
+thread_local char t_err[512] = "";
+
+lf_status fail(lf_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(t_err, sizeof(t_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int n_bpf_of(const lf_geom& g) { return (g.tokens_per_frame + g.block_size - 1) / g.block_size; }
+
+// Geometry checks shared by the device calls (d must be 64 or 128).
+lf_status check_geom(const lf_geom& g, const char* fn) {
+  if (g.B < 1 || g.H < 1) return fail(LF_ERR_INVALID_ARG, "%s: B and H must be >= 1", fn);
+  if (g.tokens_per_frame < 1 || g.tokens_per_frame > 65536)
+    return fail(LF_ERR_INVALID_ARG, "%s: tokens_per_frame must be in [1, 65536]", fn);
+  if (g.block_size < 1 || g.block_size > g.tokens_per_frame)
+    return fail(LF_ERR_INVALID_ARG, "%s: block_size must be in [1, tokens_per_frame]", fn);
+  if (g.d < 1) return fail(LF_ERR_INVALID_ARG, "%s: d must be >= 1", fn);
+  if (g.d != 64 && g.d != 128) return fail(LF_ERR_UNSUPPORTED, "%s: d=%d unsupported (64 or 128)", fn, g.d);
+  return LF_OK;
+}
+
+bool fits_int(long long v) { return v >= 0 && v <= 0x7fffffffLL; }
+
+// Clears an error left by earlier, unrelated HIP work so it is not reported as ours.
+void pending_error() { (void)hipGetLastError(); }
+
+lf_status hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return LF_OK;
+  return fail(LF_ERR_HIP, "%s: HIP error %d (%s)", fn, static_cast<int>(e), hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lf_last_error(void) { return t_err; }
+
+int32_t lf_abi_version(void) { return LF_ABI_VERSION; }
+
+lf_status lf_cag_schedule(int32_t n_chunks, int32_t T, double s_base, double s_target,
+                          const double* chunk_flops, const double* alpha, double* s_out,
+                          double* beta_out) {
+  const char* fn = "lf_cag_schedule";
+  if (n_chunks < 2 || n_chunks > 4096) return fail(LF_ERR_INVALID_ARG, "%s: n_chunks must be in [2, 4096]", fn);
+  if (T < 1) return fail(LF_ERR_INVALID_ARG, "%s: T must be >= 1", fn);
+  if (!(s_base > 0.0 && s_base < 1.0)) return fail(LF_ERR_INVALID_ARG, "%s: s_base must be in (0, 1)", fn);
+  if (!(s_target >= 0.0 && s_target < 1.0)) return fail(LF_ERR_INVALID_ARG, "%s: s_target must be in [0, 1)", fn);
+  if (!chunk_flops || !s_out || !beta_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  for (int i = 0; i < n_chunks; ++i) {
+    if (!(std::isfinite(chunk_flops[i]) && chunk_flops[i] > 0.0))
+      return fail(LF_ERR_INVALID_ARG, "%s: chunk_flops[%d] must be finite and > 0", fn, i);
+    if (alpha && !(std::isfinite(alpha[i]) && alpha[i] >= 0.0))
+      return fail(LF_ERR_INVALID_ARG, "%s: alpha[%d] must be finite and >= 0", fn, i);
+  }
+  // Total FLOP constraint sum_i F_i s_i = s_target sum_i F_i with s_1 = 0 and
+  // s_i = s_base - alpha_i beta (i >= 2), solved for beta in closed form.
+  double f_all = 0.0, f_sparse = 0.0, f_alpha = 0.0;
+  for (int i = 0; i < n_chunks; ++i) {
+    const double a = alpha ? alpha[i] : 1.0 / std::sqrt(static_cast<double>(i + 1) * T);
+    f_all += chunk_flops[i];
+    if (i > 0) {
+      f_sparse += chunk_flops[i];
+      f_alpha += chunk_flops[i] * a;
+    }
+  }
+  if (!(f_alpha > 0.0)) return fail(LF_ERR_INVALID_ARG, "%s: alpha_i is zero for every sparse chunk", fn);
+  const double beta = (s_base * f_sparse - s_target * f_all) / f_alpha;
+  double s[4096];
+  s[0] = 0.0;
+  for (int i = 1; i < n_chunks; ++i) {
+    const double a = alpha ? alpha[i] : 1.0 / std::sqrt(static_cast<double>(i + 1) * T);
+    s[i] = s_base - a * beta;
+  }
+  if (beta < 0.0) return fail(LF_ERR_INFEASIBLE, "%s: target needs beta=%g < 0", fn, beta);
+  for (int i = 1; i < n_chunks; ++i)
+    if (!(s[i] >= 0.0 && s[i] < 1.0))
+      return fail(LF_ERR_INFEASIBLE, "%s: s_%d=%g outside [0, 1)", fn, i + 1, s[i]);
+  for (int i = 0; i < n_chunks; ++i) s_out[i] = s[i];
+  *beta_out = beta;
+  return LF_OK;
+}
+
+lf_status lf_block_budget(double s, int32_t n_kblocks, int32_t W_f, int32_t n_bpf, int32_t* k_b_out) {
+  const char* fn = "lf_block_budget";
+  if (!(s >= 0.0 && s <= 1.0)) return fail(LF_ERR_INVALID_ARG, "%s: s must be in [0, 1]", fn);
+  if (n_kblocks < 1 || W_f < 1 || n_bpf < 1) return fail(LF_ERR_INVALID_ARG, "%s: sizes must be >= 1", fn);
+  if (!k_b_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  const double x = (1.0 - s) * static_cast<double>(n_kblocks) / static_cast<double>(W_f);
+  double kb = std::floor(x + 0.5);
+  if (kb < 1.0) kb = 1.0;
+  if (kb > n_bpf) kb = n_bpf;
+  *k_b_out = static_cast<int32_t>(kb);
+  return LF_OK;
+}
+
+lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float* blk_out,
+                  float* frm_out, void* stream) {
+  const char* fn = "lf_pool";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (dt != LF_FP32 && dt != LF_BF16) return fail(LF_ERR_UNSUPPORTED, "%s: dtype %d unsupported", fn, (int)dt);
+  if (n_frames < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_frames must be >= 1", fn);
+  if (!x || !blk_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(x) || !aligned16(blk_out) || (frm_out && !aligned16(frm_out)))
+    return fail(LF_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const int n_bpf = n_bpf_of(g);
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  if (!fits_int(BH * n_frames * n_bpf) || !fits_int(static_cast<long long>(n_frames) * g.tokens_per_frame))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  pending_error();
+  return hip_status(lf::launch_pool(x, dt == LF_BF16, g.d, static_cast<int>(BH), n_frames,
+                                    g.tokens_per_frame, g.block_size, n_bpf, blk_out, frm_out,
+                                    static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
+                           int32_t n_kframes, const int32_t* mem, int32_t n_mem,
+                           const int32_t* forced, int32_t n_forced, int32_t k_f,
+                           int32_t* frames_out, void* stream) {
+  const char* fn = "lf_select_frames";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (n_qb < 1 || n_kframes < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_qb and n_kframes must be >= 1", fn);
+  if (n_kframes > 256) return fail(LF_ERR_UNSUPPORTED, "%s: n_kframes=%d > 256", fn, n_kframes);
+  if (n_mem < 0 || n_forced < 0 || k_f < 0) return fail(LF_ERR_INVALID_ARG, "%s: negative count", fn);
+  if ((n_mem > 0 && !mem) || (n_forced > 0 && !forced))
+    return fail(LF_ERR_INVALID_ARG, "%s: NULL frame-id array", fn);
+  if (!q_blk || !k_frm || !frames_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q_blk) || !aligned16(k_frm) || (reinterpret_cast<uintptr_t>(frames_out) & 3u))
+    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  lf::FrameSets sets = {};
+  for (int i = 0; i < n_mem; ++i) {
+    const int f = mem[i];
+    if (f < 0 || f >= n_kframes) return fail(LF_ERR_INVALID_ARG, "%s: mem[%d]=%d out of range", fn, i, f);
+    if ((sets.mem[f >> 6] >> (f & 63)) & 1ull) return fail(LF_ERR_INVALID_ARG, "%s: duplicate memory frame %d", fn, f);
+    sets.mem[f >> 6] |= 1ull << (f & 63);
+  }
+  for (int i = 0; i < n_forced; ++i) {
+    const int f = forced[i];
+    if (f < 0 || f >= n_kframes) return fail(LF_ERR_INVALID_ARG, "%s: forced[%d]=%d out of range", fn, i, f);
+    if ((sets.forced[f >> 6] >> (f & 63)) & 1ull) return fail(LF_ERR_INVALID_ARG, "%s: duplicate forced frame %d", fn, f);
+    if ((sets.mem[f >> 6] >> (f & 63)) & 1ull)
+      return fail(LF_ERR_INVALID_ARG, "%s: frame %d is both forced and in the memory set", fn, f);
+    sets.forced[f >> 6] |= 1ull << (f & 63);
+  }
+  const int k_eff = k_f < n_mem ? k_f : n_mem;
+  const int W_f = n_forced + k_eff;
+  if (W_f < 1) return fail(LF_ERR_INVALID_ARG, "%s: empty frame set (W_f = 0)", fn);
+  const long long rows = static_cast<long long>(g.B) * g.H * n_qb;
+  if (!fits_int(rows + 3)) return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  pending_error();
+  return hip_status(lf::launch_select_frames(q_blk, k_frm, g.d, static_cast<int>(rows), n_qb, n_kframes,
+                                             sets, k_eff, W_f, frames_out,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, int32_t n_qb,
+                           int32_t n_kframes, const int32_t* frames, int32_t W_f, int32_t k_b,
+                           int32_t* blocks_out, void* stream) {
+  const char* fn = "lf_select_blocks";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (n_qb < 1 || n_kframes < 1 || W_f < 1 || k_b < 1)
+    return fail(LF_ERR_INVALID_ARG, "%s: n_qb, n_kframes, W_f and k_b must be >= 1", fn);
+  if (n_kframes > 65535) return fail(LF_ERR_UNSUPPORTED, "%s: n_kframes=%d > 65535", fn, n_kframes);
+  const int n_bpf = n_bpf_of(g);
+  if (n_bpf > 64) return fail(LF_ERR_UNSUPPORTED, "%s: %d blocks per frame > 64", fn, n_bpf);
+  if (!q_blk || !k_blk || !frames || !blocks_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q_blk) || !aligned16(k_blk) || (reinterpret_cast<uintptr_t>(frames) & 3u) ||
+      (reinterpret_cast<uintptr_t>(blocks_out) & 3u))
+    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  const int kb_eff = k_b < n_bpf ? k_b : n_bpf;
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  const long long tiles = (n_qb + 63) / 64;
+  if (!fits_int(BH * n_kframes * tiles) || !fits_int(static_cast<long long>(W_f) * kb_eff))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  pending_error();
+  return hip_status(lf::launch_select_blocks(q_blk, k_blk, frames, g.d, static_cast<int>(BH), n_qb,
+                                             n_kframes, n_bpf, W_f, k_b, kb_eff, blocks_out,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, lf_dtype dt,
+                         lf_geom g, int32_t n_qframes, int32_t n_kframes, const int32_t* blocks,
+                         int32_t W_b, float scale, void* stream) {
+  const char* fn = "lf_sparse_attn";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (dt != LF_FP32 && dt != LF_BF16) return fail(LF_ERR_UNSUPPORTED, "%s: dtype %d unsupported", fn, (int)dt);
+  if (dt == LF_BF16 && g.block_size > 64)
+    return fail(LF_ERR_UNSUPPORTED, "%s: bf16 path needs block_size <= 64", fn);
+  if (dt == LF_FP32 && g.block_size > 128)
+    return fail(LF_ERR_UNSUPPORTED, "%s: fp32 path needs block_size <= 128", fn);
+  if (n_qframes < 1 || n_kframes < 1 || W_b < 1)
+    return fail(LF_ERR_INVALID_ARG, "%s: n_qframes, n_kframes and W_b must be >= 1", fn);
+  if (!std::isfinite(scale)) return fail(LF_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (!q || !k || !v || !o || !blocks) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(blocks) & 3u))
+    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  const int n_bpf = n_bpf_of(g);
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  const long long n_qb = static_cast<long long>(n_qframes) * n_bpf;
+  const long long n_kb = static_cast<long long>(n_kframes) * n_bpf;
+  const long long lq = static_cast<long long>(n_qframes) * g.tokens_per_frame;
+  const long long lk = static_cast<long long>(n_kframes) * g.tokens_per_frame;
+  if (!fits_int(BH * n_qb) || !fits_int(n_kb) || !fits_int(lq) || !fits_int(lk))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  lf::AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.blocks = blocks;
+  a.BH = static_cast<int>(BH); a.n_qb = static_cast<int>(n_qb); a.n_kb = static_cast<int>(n_kb);
+  a.W_b = W_b; a.tpf = g.tokens_per_frame; a.bs = g.block_size; a.n_bpf = n_bpf;
+  a.lq = static_cast<int>(lq); a.lk = static_cast<int>(lk);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  pending_error();
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(dt == LF_BF16 ? lf::launch_attn_bf16(a, g.d, st) : lf::launch_attn_f32(a, g.d, st), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every symbol the
+header declares, solves the CAG schedule and the block budget like the oracle, and
+rejects bad arguments before anything is launched."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_attention_autoregressive_amd as lf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+lib_missing = not os.path.exists(lf.library_path())
+pytestmark = pytest.mark.skipif(lib_missing, reason="liblf.so not built")
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "lf.h")).read()
+    return sorted(set(re.findall(r"\b(lf_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(lf.library_path())
+    names = _declared()
+    assert {"lf_pool", "lf_select_frames", "lf_select_blocks", "lf_sparse_attn",
+            "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lf.lf_abi_version() == 1
+
+
+@pytest.mark.parametrize("n,T,s_base,s_t", [(7, 4, 0.95, 0.8), (7, 4, 0.95, 0.85), (5, 2, 0.9, 0.6),
+                                            (12, 8, 0.97, 0.75), (2, 4, 0.95, 0.4)])
+def test_cag_matches_oracle(n, T, s_base, s_t):
+    rng = np.random.default_rng(n + T)
+    for F in (list(range(1, n + 1)), rng.uniform(0.5, 3, n).cumsum().tolist()):
+        s_lib, b_lib = lf.lf_cag_schedule(n, T, s_base, s_t, F)
+        s_or, b_or = oracle.cag_schedule(n, T, s_base, s_t, F)
+        assert b_lib == pytest.approx(b_or, rel=1e-12, abs=1e-14)
+        assert np.allclose(s_lib, s_or, rtol=0, atol=1e-12)
+        alpha = rng.uniform(0.1, 0.5, n).tolist()
+        try:
+            s_or, b_or = oracle.cag_schedule(n, T, s_base, s_t, F, alpha=alpha)
+        except ValueError:
+            with pytest.raises(lf.LfError):
+                lf.lf_cag_schedule(n, T, s_base, s_t, F, alpha=alpha)
+            continue
+        s_lib, b_lib = lf.lf_cag_schedule(n, T, s_base, s_t, F, alpha=alpha)
+        assert b_lib == pytest.approx(b_or, rel=1e-12, abs=1e-14)
+        assert np.allclose(s_lib, s_or, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("s_t", [0.93, 0.2])
+def test_cag_infeasible(s_t):
+    with pytest.raises(lf.LfError) as e:
+        lf.lf_cag_schedule(7, 4, 0.95, s_t, list(range(1, 8)))
+    assert e.value.status == lf.LF_ERR_INFEASIBLE
+
+
+@pytest.mark.parametrize("args", [(1, 4, 0.95, 0.8), (7, 0, 0.95, 0.8), (7, 4, 1.5, 0.8),
+                                  (7, 4, 0.95, 1.0), (7, 4, 0.95, -0.1)])
+def test_cag_invalid(args):
+    n = max(args[0], 1)
+    with pytest.raises(lf.LfError) as e:
+        lf.lf_cag_schedule(*args, list(range(1, n + 1)))
+    assert e.value.status == lf.LF_ERR_INVALID_ARG
+    with pytest.raises(lf.LfError):
+        lf.lf_cag_schedule(3, 4, 0.95, 0.5, [1.0, -2.0, 3.0])
+
+
+def test_block_budget_matches_oracle():
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        s = float(rng.uniform(0, 1))
+        n_kb, W_f, n_bpf = int(rng.integers(1, 3000)), int(rng.integers(1, 30)), int(rng.integers(1, 64))
+        assert lf.lf_block_budget(s, n_kb, W_f, n_bpf) == oracle.block_budget(s, n_kb, W_f, n_bpf)
+    # exact half-way points round up
+    assert lf.lf_block_budget(0.5, 10, 2, 25) == 3
+    with pytest.raises(lf.LfError):
+        lf.lf_block_budget(1.5, 10, 2, 25)
+
+
+# --------------------------------------------------------------------- argument validation
+_lib = None
+
+
+def _c():
+    global _lib
+    if _lib is None:
+        lf._load()
+        _lib = lf._lib
+    return _lib
+
+
+FAKE = 0x10000            # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _err(status, want):
+    assert status == want, (status, _c().lf_last_error().decode())
+    assert _c().lf_last_error().decode() != ""
+
+
+def test_pool_validation():
+    c = _c()
+    good = lf.Geom(1, 2, 128, 1560, 64)
+    _err(c.lf_pool(FAKE, 1, lf.Geom(1, 2, 96, 1560, 64), 3, FAKE, None, None), lf.LF_ERR_UNSUPPORTED)
+    _err(c.lf_pool(FAKE, 7, good, 3, FAKE, None, None), lf.LF_ERR_UNSUPPORTED)
+    _err(c.lf_pool(None, 1, good, 3, FAKE, None, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool(FAKE + 4, 1, good, 3, FAKE, None, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool(FAKE, 1, good, 0, FAKE, None, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool(FAKE, 1, lf.Geom(0, 2, 128, 1560, 64), 3, FAKE, None, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool(FAKE, 1, lf.Geom(1, 2, 128, 64, 65), 3, FAKE, None, None), lf.LF_ERR_INVALID_ARG)
+
+
+def test_select_frames_validation():
+    c = _c()
+    g = lf.Geom(1, 2, 128, 1560, 64)
+    arr = lf._i32_array
+
+    def call(mem, forced, k_f=2, n_kf=10, out=FAKE):
+        return c.lf_select_frames(FAKE, FAKE, g, 75, n_kf, arr(mem), len(mem), arr(forced),
+                                  len(forced), k_f, out, None)
+
+    _err(call([1, 2], [2, 9]), lf.LF_ERR_INVALID_ARG)          # overlap
+    _err(call([1, 1], [0]), lf.LF_ERR_INVALID_ARG)             # duplicate
+    _err(call([1, 12], [0]), lf.LF_ERR_INVALID_ARG)            # out of range
+    _err(call([], [], k_f=3), lf.LF_ERR_INVALID_ARG)           # empty T_r
+    _err(call([1], [0], k_f=-1), lf.LF_ERR_INVALID_ARG)
+    _err(call([1], [0], n_kf=300), lf.LF_ERR_UNSUPPORTED)
+    _err(call([1], [0], out=FAKE + 2), lf.LF_ERR_INVALID_ARG)
+
+
+def test_select_blocks_validation():
+    c = _c()
+    g = lf.Geom(1, 2, 128, 1560, 64)
+    _err(c.lf_select_blocks(FAKE, FAKE, g, 75, 21, FAKE, 8, 0, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_select_blocks(FAKE, FAKE, g, 75, 21, FAKE, 0, 8, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_select_blocks(FAKE, FAKE, lf.Geom(1, 2, 128, 1560, 16), 75, 21, FAKE, 8, 8, FAKE, None),
+         lf.LF_ERR_UNSUPPORTED)                                 # 98 blocks per frame
+    _err(c.lf_select_blocks(None, FAKE, g, 75, 21, FAKE, 8, 8, FAKE, None), lf.LF_ERR_INVALID_ARG)
+
+
+def test_sparse_attn_validation():
+    c = _c()
+    g = lf.Geom(1, 2, 128, 1560, 64)
+    F = FAKE
+    _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 128, 1560, 128), 3, 21, F, 64, 0.1, None),
+         lf.LF_ERR_UNSUPPORTED)                                 # bf16 path needs bs <= 64
+    _err(c.lf_sparse_attn(F, F, F, F, 1, g, 3, 21, F, 0, 0.1, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_sparse_attn(F, F, F, F, 1, g, 3, 21, F, 64, math.inf, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_sparse_attn(F, F, None, F, 1, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_sparse_attn(F, F, F, F + 8, 1, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_sparse_attn(F, F, F, F, 3, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_UNSUPPORTED)
+    _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 80, 1560, 64), 3, 21, F, 64, 0.1, None),
+         lf.LF_ERR_UNSUPPORTED)
+
+
+def test_error_message_is_per_thread():
+    import threading
+    c = _c()
+    _err(c.lf_pool(None, 1, lf.Geom(1, 2, 128, 1560, 64), 3, FAKE, None, None), lf.LF_ERR_INVALID_ARG)
+    seen = {}
+
+    def other():
+        seen["msg"] = c.lf_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "lf_pool" in c.lf_last_error().decode()

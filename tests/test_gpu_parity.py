@@ -1,0 +1,187 @@
+"""GPU parity of the whole HSA path (C ABI -> HIP kernels) against the CPU oracle.
+
+Workloads: the tiny fp32 case (every row, every output), the 480p chunk-2 and chunk-7
+layers and the 69-frame LongLive-like layer at full size (masks on every row; attention
+on a sample of rows that covers two whole heads, every ragged query block and random
+rows), plus edge cases (ragged and 1-token blocks, d=64, dense lists, skipped ids,
+empty memory set, k >= candidates) and bitwise determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_attention_autoregressive_amd as lf
+from support import (compare_attention, compare_masks, lib_k_b, log, oracle_k_b, run_gpu,
+                     run_oracle_masks, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _case(name):
+    """(workload, inputs, fp64 arrays, gpu results, oracle masks, k_b) -- computed once."""
+    if name in _cache:
+        return _cache[name]
+    w = synth.WORKLOADS[name]
+    log(f"[case] {name}: generating inputs")
+    x = synth.make(w)
+    q64, k64, v64 = x.np64()
+    k_b = lib_k_b(w)
+    assert k_b == oracle_k_b(w)
+    gpu = run_gpu(w, x, k_b)
+    log(f"[case] {name}: oracle masks")
+    ref = run_oracle_masks(w, q64, k64, k_b)
+    _cache[name] = (w, x, (q64, k64, v64), gpu, ref, k_b)
+    return _cache[name]
+
+
+ALL = ["tiny_fp32", "480p_chunk2of7", "480p_chunk7of7", "longlive_69f"]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_pool_parity(name):
+    w, x, (q64, k64, v64), gpu, ref, k_b = _case(name)
+    for key in ("q_blk", "k_blk", "k_frm"):
+        e = ref[key]
+        err = np.abs(gpu[key].astype(np.float64) - e).max() / np.abs(e).max()
+        log(f"[pool] {name} {key}: max rel err {err:.2e}")
+        assert err <= 2e-6, (key, err)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_mask_parity(name):
+    w, x, (q64, k64, v64), gpu, ref, k_b = _case(name)
+    nb = ref["n_bpf"]
+    stats = compare_masks(gpu, ref, min(k_b, nb))
+    log(f"[mask] {name}: {stats}")
+    W_f = len(w.forced) + min(w.k_f, len(w.mem))
+    assert gpu["frames"].shape[-1] == W_f
+    # forced frames always present; every row's count is the budget
+    fr = gpu["frames"].reshape(-1, W_f)
+    for f in w.forced:
+        assert (fr == f).any(axis=1).all()
+    assert gpu["blocks"].shape[-1] == W_f * min(k_b, nb)
+    assert stats["frame_ties"] + stats["block_ties"] <= max(2, stats["rows"] // 100)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_attention_parity(name):
+    w, x, (q64, k64, v64), gpu, ref, k_b = _case(name)
+    rows = sample_rows(w, gpu["frames"].shape[2], full=(w.H * gpu["frames"].shape[2] <= 1000 and w.n_kframes <= 8))
+    res = compare_attention(w, gpu, q64, k64, v64, rows, w.dtype)
+    log(f"[attn] {name}: {res}")
+
+
+def test_planted_frames_recovered_on_gpu():
+    w, x, _, gpu, _, _ = _case("longlive_69f")
+    fr = gpu["frames"][0]
+    hit = [set(x.pairs[0, h, r].tolist()) <= set(fr[h, r].tolist())
+           for h in range(w.H) for r in range(fr.shape[1])]
+    assert np.mean(hit) >= 0.99
+
+
+def test_determinism_bitwise():
+    w = synth.CHUNK7
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    a = run_gpu(w, x, w.k_b, q, k, v)
+    b = run_gpu(w, x, w.k_b, q, k, v)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+# ------------------------------------------------------------------------------ edge cases
+def _edge(w, k_b=None, full=True):
+    x = synth.make(w)
+    q64, k64, v64 = x.np64()
+    k_b = w.k_b if k_b is None else k_b
+    gpu = run_gpu(w, x, k_b)
+    ref = run_oracle_masks(w, q64, k64, k_b)
+    stats = compare_masks(gpu, ref, min(k_b, ref["n_bpf"]))
+    rows = sample_rows(w, gpu["frames"].shape[2], full=full)
+    res = compare_attention(w, gpu, q64, k64, v64, rows, w.dtype)
+    log(f"[edge] {w.name}: {stats} {res}")
+    return x, gpu, ref
+
+
+def _base(**kw):
+    from dataclasses import replace
+    w = replace(synth.CHUNK7, H=2, tpf=200, n_kframes=9, current=(6, 7, 8), sink=(0,), recent=(5,),
+                mem=(1, 2, 3, 4), k_f=2, k_b=2, q_pool=(0, 1, 2, 3, 4), name="edge_base", seed=7001)
+    return replace(w, **kw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_edge_ragged_blocks(dtype):
+    # 200 tokens per frame in blocks of 64 -> 64, 64, 64, 8; several tiles and a ragged tail
+    _edge(_base(dtype=dtype, name=f"ragged_{dtype}"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_edge_one_token_blocks(dtype):
+    # 17 tokens per frame in blocks of 16 -> 16 + 1: 1-token query and key blocks
+    _edge(_base(dtype=dtype, tpf=17, bs=16, k_b=1, name=f"onetoken_{dtype}", seed=7002))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_edge_head_dim_64(dtype):
+    _edge(_base(dtype=dtype, d=64, bs=32, k_b=3, name=f"d64_{dtype}", seed=7003))
+
+
+def test_edge_all_candidates_kept_equals_dense():
+    # k_f >= |M| and k_b >= n_bpf: every block listed -> dense attention
+    w = _base(k_f=9, k_b=9, name="dense_lists", seed=7004)
+    x, gpu, ref = _edge(w)
+    q64, k64, v64 = x.np64()
+    dense = oracle.dense_attn(q64, k64, v64, w.scale)
+    err = np.abs(gpu["o"] - dense).max()
+    assert err <= 2e-2, err
+
+
+def test_edge_first_chunk_no_memory():
+    # chunk 1 under CAG: no history, the chunk's own frames forced, dense within them
+    w = _base(n_kframes=3, current=(0, 1, 2), sink=(0,), recent=(), mem=(), k_f=4, k_b=25,
+              q_pool=(0, 1, 2), name="first_chunk", seed=7005)
+    _edge(w)
+
+
+def test_edge_k_f_zero_and_batch():
+    w = _base(B=2, k_f=0, name="kf0_batch2", seed=7006)
+    _edge(w)
+
+
+def test_edge_skipped_ids():
+    # ids outside [0, n_kb) in a list are skipped: same as the list without them
+    w = _base(name="skipped_ids", seed=7007)
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    nb = lf.n_bpf(g)
+    n_qb, n_kb = 3 * nb, w.n_kframes * nb
+    rng = np.random.default_rng(0)
+    lists = np.sort(np.stack([rng.choice(n_kb, 6, replace=False) for _ in range(w.H * n_qb)]), axis=1)
+    noisy = lists.copy()
+    noisy[:, 0] = -5
+    noisy[:, 3] = n_kb + 7
+    blk = torch.as_tensor(noisy.reshape(1, w.H, n_qb, 6), dtype=torch.int32, device=dev)
+    o = lf.lf_sparse_attn(q, k, v, g, 3, w.n_kframes, blk, w.scale)
+    keep = np.concatenate([lists[:, 1:3], lists[:, 4:]], axis=1).reshape(1, w.H, n_qb, 4)
+    q64, k64, v64 = x.np64()
+    ref = oracle.sparse_attn(q64, k64, v64, keep, w.tpf, w.bs, w.scale)
+    assert np.abs(o.float().cpu().numpy() - ref).max() <= 2e-2
+
+
+def test_edge_constant_values():
+    # constant V -> every output equals that constant, up to one bf16 ulp (P is rounded
+    # to bf16 for the matrix cores, the normaliser is summed in fp32)
+    w = _base(name="constV", seed=7008)
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    v = torch.full_like(x.v, 0.8125).to(dev)           # exactly representable in bf16
+    gpu = run_gpu(w, x, w.k_b, v=v)
+    assert np.abs(gpu["o"] - 0.8125).max() <= 2.0 ** -8
