@@ -116,7 +116,7 @@ lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float
  * q_blk: [B, H, n_qb, d] fp32 (lf_pool of the queries). k_frm: [B, H, n_kframes, d]
  *   fp32 (frame means of all key frames; only those in M are read).
  * mem, forced: HOST arrays of frame ids (n_mem, n_forced entries), each id in
- *   [0, n_kframes), no duplicates, the two sets disjoint; n_forced + n_mem >= 1.
+ *   [0, n_kframes), no duplicates, the two sets disjoint; W_f (below) must be >= 1.
  * frames_out: [B, H, n_qb, W_f] int32, W_f = n_forced + min(k_f, n_mem), each row
  *   ascending.
  * Limits: d in {64, 128}; n_kframes <= 256; k_f >= 0.
@@ -135,8 +135,8 @@ lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, in
  * block ids tau*n_bpf + j.
  * q_blk: [B, H, n_qb, d] fp32. k_blk: [B, H, n_kframes*n_bpf, d] fp32.
  * frames: [B, H, n_qb, W_f] int32 device array, each row ascending and unique with ids
- *   in [0, n_kframes) (the output of lf_select_frames). Ids out of range are skipped
- *   (their list slots are left holding -1) rather than read.
+ *   in [0, n_kframes) (the output of lf_select_frames). A row breaking this gets
+ *   unspecified list entries; nothing outside the buffers is read or written.
  * blocks_out: [B, H, n_qb, W_f*min(k_b, n_bpf)] int32.
  * Limits: d in {64, 128}; n_bpf <= 64; n_kframes <= 65535; k_b >= 1; W_f >= 1.
  * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_HIP.
@@ -154,6 +154,7 @@ lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, in
  * blocks: [B, H, n_qb, W_b] int32 device array, n_qb = n_qframes*n_bpf; ids should be
  *   unique (a repeated id is counted twice); ids outside [0, n_kframes*n_bpf) are
  *   skipped. A row with no valid id produces zeros.
+ * scale: the softmax scale (usually 1/sqrt(d)); finite and > 0.
  * LF_BF16 runs on bf16 matrix cores (fp32 accumulate and softmax) and needs d = 128 or
  *   64 and bs <= 64; LF_FP32 runs in fp32 on the vector units and needs d in {64, 128}
  *   and bs <= 128.

@@ -166,11 +166,12 @@ lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, in
   const int k_eff = k_f < n_mem ? k_f : n_mem;
   const int W_f = n_forced + k_eff;
   if (W_f < 1) return fail(LF_ERR_INVALID_ARG, "%s: empty frame set (W_f = 0)", fn);
-  const long long rows = static_cast<long long>(g.B) * g.H * n_qb;
-  if (!fits_int(rows + 3)) return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  if (!fits_int(BH * ((n_qb + 15) / 16)) || !fits_int(BH * n_qb))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   pending_error();
-  return hip_status(lf::launch_select_frames(q_blk, k_frm, g.d, static_cast<int>(rows), n_qb, n_kframes,
-                                             sets, k_eff, W_f, frames_out,
+  return hip_status(lf::launch_select_frames(q_blk, k_frm, g.d, static_cast<int>(BH), n_qb, n_kframes,
+                                             sets, n_mem, k_eff, W_f, frames_out,
                                              static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -191,12 +192,12 @@ lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, in
     return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
   const int kb_eff = k_b < n_bpf ? k_b : n_bpf;
   const long long BH = static_cast<long long>(g.B) * g.H;
-  const long long tiles = (n_qb + 63) / 64;
+  const long long tiles = (n_qb + 15) / 16;
   if (!fits_int(BH * n_kframes * tiles) || !fits_int(static_cast<long long>(W_f) * kb_eff))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   pending_error();
   return hip_status(lf::launch_select_blocks(q_blk, k_blk, frames, g.d, static_cast<int>(BH), n_qb,
-                                             n_kframes, n_bpf, W_f, k_b, kb_eff, blocks_out,
+                                             n_kframes, n_bpf, W_f, kb_eff, blocks_out,
                                              static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -213,7 +214,8 @@ lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, l
     return fail(LF_ERR_UNSUPPORTED, "%s: fp32 path needs block_size <= 128", fn);
   if (n_qframes < 1 || n_kframes < 1 || W_b < 1)
     return fail(LF_ERR_INVALID_ARG, "%s: n_qframes, n_kframes and W_b must be >= 1", fn);
-  if (!std::isfinite(scale)) return fail(LF_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(LF_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
   if (!q || !k || !v || !o || !blocks) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(blocks) & 3u))

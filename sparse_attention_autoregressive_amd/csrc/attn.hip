@@ -113,8 +113,26 @@ __global__ void __launch_bounds__(128) attn_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------------- bf16
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): inside each group of 16 lanes, lane
+// c receives element (c % 4) of the 8-byte words addressed by lanes c/4, 4 + c/4,
+// 8 + c/4 and 12 + c/4, i.e. lane 4r + q supplies row r, columns 4q..4q+3 of a 4 x 16
+// tile of 16-bit values and lane c gets column c.
+__device__ __forceinline__ uint2 ds_read_tr16(const lds_u8* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Running-max slack (log2 units): the O accumulator and row sum are rescaled only when
+// a tile's maximum exceeds the max in use by more than this, so p = 2^(x - m) <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D>
-__global__ void __launch_bounds__(128) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 16;                  // MFMA k-steps over d (S^T)
   constexpr int DT = D / 32;                  // 32-wide d tiles (O^T)
   constexpr int CH = D / 8;                   // 16-byte chunks per token row
@@ -154,7 +172,27 @@ __global__ void __launch_bounds__(128) attn_bf16_kernel(AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
-  float m = -1e30f, lsum = 0.f;
+  float m = -1e30f, lsum = 0.f;   // max in use (scaled log2 units) and partial row sum
+  const float c = a.scale_log2;
+
+  // per-lane byte offsets inside a tile, independent of the tile
+  int k_off[KS];                              // K A-operand: row j, chunk 2s+g (swizzled)
+#pragma unroll
+  for (int s = 0; s < KS; ++s) k_off[s] = j * ROWB + (((2 * s + g) ^ (j & (CH - 1))) * 16);
+  // V^T A-operand via transposing reads: this lane supplies row 16ks + 8h + 4g + (l%16)/4,
+  // columns 32dt + 16((l/16)%2) + 4(l%4) .. +3
+  const int grp = l / 16, i16 = l % 16;
+  int v_off[DT][2][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = 16 * ks + 8 * h + 4 * g + i16 / 4;
+        const int d = 32 * dt + 16 * (grp % 2) + 4 * (i16 % 4);
+        v_off[dt][ks][h] = key * ROWB + (((d / 8) ^ (key & (CH - 1))) * 16) + (d % 8) * 2;
+      }
 
   const int* bl = a.blocks + static_cast<size_t>(work) * a.W_b;
   auto ok = [&](int e) {
@@ -168,8 +206,8 @@ __global__ void __launch_bounds__(128) attn_bf16_kernel(AttnArgs a) {
       const int base = (i * 2 + w) * 1024;    // wave-uniform LDS offset
       const int off = base + l * 16;
       const int row = off / ROWB;
-      const int c = ((off % ROWB) / 16) ^ (row & (CH - 1));
-      const size_t src = static_cast<size_t>(tok0 + min(row, nv - 1)) * D + c * 8;
+      const int cc = ((off % ROWB) / 16) ^ (row & (CH - 1));
+      const size_t src = static_cast<size_t>(tok0 + min(row, nv - 1)) * D + cc * 8;
       __builtin_amdgcn_global_load_lds(Kg + src, (__attribute__((address_space(3))) void*)(&smem[buf][0][base]), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(Vg + src, (__attribute__((address_space(3))) void*)(&smem[buf][1][base]), 16, 0, 0);
     }
@@ -200,59 +238,67 @@ __global__ void __launch_bounds__(128) attn_bf16_kernel(AttnArgs a) {
     }
 
     if (nq > 0) {
-      const unsigned char* Kt = smem[buf][0];
-      const unsigned char* Vt = smem[buf][1];
+      const lds_u8* Kt = (const lds_u8*)(&smem[buf][0][0]);
+      const lds_u8* Vt = (const lds_u8*)(&smem[buf][1][0]);
       f32x16 sacc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int c = (2 * s + g) ^ (j & (CH - 1));
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kt + j * ROWB + c * 16);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>((const unsigned char*)(Kt + k_off[s]));
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
       }
-      // sacc[v] = S^T[key 8(v/4) + 4g + v%4][query j]
-      float x[16];
-      float mt = -INFINITY;
+      // sacc[v] = S^T[key 8(v/4) + 4g + v%4][query j]; scale > 0, so the max of the raw
+      // scores gives the max of the scaled ones
+      if (nv < 32) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = 8 * (v / 4) + 4 * g + (v % 4);
-        x[v] = key < nv ? sacc[v] * a.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[v]);
+        for (int v = 0; v < 16; ++v)
+          if (8 * (v / 4) + 4 * g + (v % 4) >= nv) sacc[v] = -INFINITY;
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m, mt);
-      const float corr = fast_exp2(m - mn);
-      m = mn;
+      float mt = sacc[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
+      const bool grow = mt > m + kRescaleSlack;
+      if (__any(grow)) {
+        const float mn = grow ? mt : m;
+        const float corr = fast_exp2(m - mn);
+        m = mn;
+        lsum *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
+      }
+      // P^T as bf16 pairs; the row sum takes the same rounded weights the matrix cores
+      // multiply, so the normalised weights sum to one (exact for a single dominant key)
+      uint32_t pw[8];
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bf16x2 pr;
+        pr[0] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i], c, -m)));
+        pr[1] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i + 1], c, -m)));
+        pw[i] = __builtin_bit_cast(uint32_t, pr);
+        ps0 += __uint_as_float(pw[i] << 16);
+        ps1 += __uint_as_float(pw[i] & 0xFFFF0000u);
+      }
+      lsum += ps0 + ps1;
       bf16x8 pb[2];
-      float ps = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = fast_exp2(x[v] - mn);
-        ps += pv;
-        pb[v / 8][v % 8] = static_cast<__bf16>(pv);
+      {
+        const u32x4 lo = {pw[0], pw[1], pw[2], pw[3]}, hi = {pw[4], pw[5], pw[6], pw[7]};
+        pb[0] = __builtin_bit_cast(bf16x8, lo);
+        pb[1] = __builtin_bit_cast(bf16x8, hi);
       }
-      lsum = lsum * corr + ps;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
-      // O^T += V^T P^T; B slot t of pb[ks] is key 16ks + 8(t/4) + 4g + t%4
+      // O^T += V^T P^T; B slot t of pb[ks] is key 16ks + 8(t/4) + 4g + t%4, and the two
+      // transposing reads give this lane's d the same keys
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + j;
-        const int cd = d / 8, ed = d % 8;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          uint32_t wv[4];
-#pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) {
-            const int k0 = 16 * ks + 8 * ((2 * t2) / 4) + 4 * g + ((2 * t2) % 4);
-            const int k1 = k0 + 1;
-            const uint16_t e0 = *reinterpret_cast<const uint16_t*>(Vt + k0 * ROWB + ((cd ^ (k0 & (CH - 1))) * 16) + ed * 2);
-            const uint16_t e1 = *reinterpret_cast<const uint16_t*>(Vt + k1 * ROWB + ((cd ^ (k1 & (CH - 1))) * 16) + ed * 2);
-            wv[t2] = static_cast<uint32_t>(e0) | (static_cast<uint32_t>(e1) << 16);
-          }
+          const uint2 lo = ds_read_tr16(Vt + v_off[dt][ks][0]);
+          const uint2 hi = ds_read_tr16(Vt + v_off[dt][ks][1]);
+          const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
           const bf16x8 va = __builtin_bit_cast(bf16x8, wv);
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], acc[dt], 0, 0, 0);
         }

@@ -15,13 +15,13 @@ struct FrameSets {
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
                        int n_bpf, float* blk, float* frm, hipStream_t st);
 
-hipError_t launch_select_frames(const float* q_blk, const float* k_frm, int d, int n_rows,
-                                int n_qb, int n_kframes, const FrameSets& sets, int k_eff,
+hipError_t launch_select_frames(const float* q_blk, const float* k_frm, int d, int BH, int n_qb,
+                                int n_kframes, const FrameSets& sets, int n_mem, int k_eff,
                                 int W_f, int* out, hipStream_t st);
 
 hipError_t launch_select_blocks(const float* q_blk, const float* k_blk, const int* frames, int d,
-                                int BH, int n_qb, int n_kframes, int n_bpf, int W_f, int k_b,
-                                int kb_eff, int* out, hipStream_t st);
+                                int BH, int n_qb, int n_kframes, int n_bpf, int W_f, int kb_eff,
+                                int* out, hipStream_t st);
 
 struct AttnArgs {
   const void* q;

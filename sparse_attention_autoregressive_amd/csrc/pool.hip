@@ -93,7 +93,8 @@ __global__ void __launch_bounds__(D) frame_means_kernel(const float* __restrict_
   const int f = blockIdx.x - bh * n_frames;
   const float* b = blk + (static_cast<size_t>(bh) * n_frames + f) * n_bpf * D + threadIdx.x;
   float sum = 0.f;
-  for (int j = 0; j < n_bpf; ++j) sum += b[j * D] * static_cast<float>(min(bs, tpf - j * bs));
+#pragma unroll 8
+  for (int j = 0; j < n_bpf; ++j) sum = fmaf(b[j * D], static_cast<float>(min(bs, tpf - j * bs)), sum);
   frm[(static_cast<size_t>(bh) * n_frames + f) * D + threadIdx.x] = sum / static_cast<float>(tpf);
 }
 

@@ -151,6 +151,7 @@ def test_sparse_attn_validation():
          lf.LF_ERR_UNSUPPORTED)                                 # bf16 path needs bs <= 64
     _err(c.lf_sparse_attn(F, F, F, F, 1, g, 3, 21, F, 0, 0.1, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_sparse_attn(F, F, F, F, 1, g, 3, 21, F, 64, math.inf, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_sparse_attn(F, F, F, F, 1, g, 3, 21, F, 64, -0.1, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_sparse_attn(F, F, None, F, 1, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_sparse_attn(F, F, F, F + 8, 1, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_sparse_attn(F, F, F, F, 3, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_UNSUPPORTED)
