@@ -72,22 +72,25 @@ def pool_bytes(w, n_frames, with_frames):
     return rd + wr
 
 
-def run_cpu_baseline(w, heads: int):
+def run_cpu_baseline(w, heads: int, min_s: float):
     """The CPU oracle (numpy fp64) on the first `heads` heads of one layer: pool, select
-    and attend. Returns (dense-equiv TFLOP/s, seconds, dense flops of the sample)."""
+    and attend, repeated until at least `min_s` seconds have passed. Returns
+    (dense-equiv TFLOP/s, seconds, repeats, dense flops of one repeat)."""
     import dataclasses
 
     import oracle
     ws = dataclasses.replace(w, H=heads)
     x = synth.make(ws)
     q64, k64, v64 = x.np64()
-    k_b = w.k_b
-    t0 = time.perf_counter()
-    out = oracle.hsa(q64, k64, v64, tpf=ws.tpf, bs=ws.bs, n_kframes=ws.n_kframes, mem=ws.mem,
-                     forced=ws.forced, k_f=ws.k_f, k_b=k_b, scale=ws.scale)
-    dt = time.perf_counter() - t0
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < min_s:
+        t0 = time.perf_counter()
+        out = oracle.hsa(q64, k64, v64, tpf=ws.tpf, bs=ws.bs, n_kframes=ws.n_kframes, mem=ws.mem,
+                         forced=ws.forced, k_f=ws.k_f, k_b=w.k_b, scale=ws.scale)
+        dt += time.perf_counter() - t0
+        reps += 1
     dense, _ = flops_of(ws, out["blocks"])
-    return dense / dt / 1e12, dt, dense
+    return dense * reps / dt / 1e12, dt, reps, dense
 
 
 def blas_threads():
@@ -106,7 +109,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="480p_chunk7of7", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layers", type=int, default=4, help="independent input sets cycled per step")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-min-s", type=float, default=10.0, help="repeat the CPU sample for at least this long")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build targets one GPU; the HSA path has no multi-GPU mode "
@@ -136,6 +142,14 @@ def main():
                                          w.seed + 100 * li, dev, pools))
     wss = [Workspace(plan, dtype, dev) for _ in sets]
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.current_stream()
 
@@ -195,10 +209,11 @@ def main():
     cpu = None
     if args.cpu_heads > 0:
         print(f"[bench] CPU oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
-        cpu_tflops, cpu_s, cpu_dense = run_cpu_baseline(w, args.cpu_heads)
+        cpu_tflops, cpu_s, reps, cpu_dense = run_cpu_baseline(w, args.cpu_heads, args.cpu_min_s)
         cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
                "sample": f"{w.name}, heads 0..{args.cpu_heads - 1} of {w.H}: pool + select + attention "
-                         f"in numpy fp64 ({cpu_dense:.3e} dense-equiv FLOP in {cpu_s:.1f} s)",
+                         f"in numpy fp64, {reps} repeats ({cpu_dense:.3e} dense-equiv FLOP each) "
+                         f"in {cpu_s:.1f} s",
                "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or platform.machine()}
 
     line = {

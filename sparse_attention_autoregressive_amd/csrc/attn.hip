@@ -130,16 +130,151 @@ __device__ __forceinline__ uint2 ds_read_tr16(const lds_u8* p) {
 // Running-max slack (log2 units): the O accumulator and row sum are rescaled only when
 // a tile's maximum exceeds the max in use by more than this, so p = 2^(x - m) <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
+// Listed blocks staged in LDS at a time (longer lists are walked in segments).
+constexpr int kListSeg = 256;
+
+// LDS layouts of the 32-token tiles (16-byte chunks XOR-swizzled per row).
+// K is read as MFMA A operands: 16 consecutive lanes take 16 consecutive rows at one
+// logical chunk, so the swizzle spreads those rows over all 16 (d = 128) chunk slots;
+// with d = 64 two rows share a 256-byte bank window, hence the (row >> 1) term.
+// V is read with transposing reads: a 32-lane half takes 4 consecutive rows at 4
+// consecutive chunks, so the swizzle moves each of the 4 rows to its own 4-chunk block.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// Per-lane state of one attention row, shared by the tile steps.
+template <int D>
+struct AttnLane {
+  static constexpr int KS = D / 16;           // MFMA k-steps over d (S^T)
+  static constexpr int DT = D / 32;           // 32-wide d tiles (O^T)
+  static constexpr int ROWB = D * 2;          // bytes per token row
+  static constexpr int TILE = 32 * ROWB;      // bytes per 32-token K (or V) tile
+  static constexpr int LOADS = TILE / (128 * 16);
+  bf16x8 qf[KS];                              // Q^T fragments (query j, d 16s + 8g ..)
+  f32x16 acc[DT];                             // O^T accumulators (query j)
+  float m, lsum;                              // max in use (scaled log2 units), row sum
+  int k_off[KS];                              // K A-operand byte offsets in a tile
+  int v_off[DT][2][2];                        // V^T transposing-read byte offsets
+  int cp_row[LOADS];                          // global -> LDS copy: tile row of this lane
+  int cp_koff[LOADS], cp_voff[LOADS];         // ... and its byte offset in a full tile
+};
+
+// Copies the 32-token K and V tiles starting at token tok0 (nv valid rows; rows past nv
+// repeat the last valid one and are masked later) from global memory straight into
+// LDS. Each wave fills 1 KB pieces 2i + w of each tile; the lane writes its 16-byte slot
+// and fetches the chunk that the tile's swizzle maps there.
+template <int D>
+__device__ __forceinline__ void issue_tile(unsigned char* k_lds, unsigned char* v_lds,
+                                           const __bf16* Kg, const __bf16* Vg, int tok0, int nv,
+                                           const AttnLane<D>& s, int w) {
+  constexpr int ROWB = AttnLane<D>::ROWB;
+  const char* kb = reinterpret_cast<const char*>(Kg + static_cast<size_t>(tok0) * D);
+  const char* vb = reinterpret_cast<const char*>(Vg + static_cast<size_t>(tok0) * D);
+  if (nv == 32) {
+#pragma unroll
+    for (int i = 0; i < AttnLane<D>::LOADS; ++i) {
+      const int base = (i * 2 + w) * 1024;    // wave-uniform LDS offset
+      __builtin_amdgcn_global_load_lds(kb + s.cp_koff[i], (__attribute__((address_space(3))) void*)(k_lds + base), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + s.cp_voff[i], (__attribute__((address_space(3))) void*)(v_lds + base), 16, 0, 0);
+    }
+  } else {                                    // short tile: clamp rows to the last valid one
+#pragma unroll
+    for (int i = 0; i < AttnLane<D>::LOADS; ++i) {
+      const int base = (i * 2 + w) * 1024;
+      const int dr = (min(s.cp_row[i], nv - 1) - s.cp_row[i]) * ROWB;
+      __builtin_amdgcn_global_load_lds(kb + s.cp_koff[i] + dr, (__attribute__((address_space(3))) void*)(k_lds + base), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + s.cp_voff[i] + dr, (__attribute__((address_space(3))) void*)(v_lds + base), 16, 0, 0);
+    }
+  }
+}
+
+// One 32-token tile of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void tile_compute(const unsigned char* Kt_, const unsigned char* Vt_,
+                                             int nv, int g, float c, AttnLane<D>& s) {
+  constexpr int KS = AttnLane<D>::KS, DT = AttnLane<D>::DT;
+  const lds_u8* Kt = (const lds_u8*)Kt_;
+  const lds_u8* Vt = (const lds_u8*)Vt_;
+  bf16x8 kf[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) kf[st] = *reinterpret_cast<const bf16x8*>((const unsigned char*)(Kt + s.k_off[st]));
+  f32x16 sacc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+  for (int st = 0; st < KS; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], s.qf[st], sacc, 0, 0, 0);
+  // V^T fragments, in flight while the softmax runs
+  uint2 vfr[DT][2][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vfr[dt][ks][h] = ds_read_tr16(Vt + s.v_off[dt][ks][h]);
+  // sacc[v] = S^T[key 8(v/4) + 4g + v%4][query j]; scale > 0, so the max of the raw
+  // scores gives the max of the scaled ones
+  if (nv < 32) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (8 * (v / 4) + 4 * g + (v % 4) >= nv) sacc[v] = -INFINITY;
+  }
+  float mt = sacc[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
+  const bool grow = mt > s.m + kRescaleSlack;
+  if (__any(grow)) {
+    const float mn = grow ? mt : s.m;
+    const float corr = fast_exp2(s.m - mn);
+    s.m = mn;
+    s.lsum *= corr;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s.acc[dt][v] *= corr;
+  }
+  // P^T as bf16 pairs; the row sum takes the same rounded weights the matrix cores
+  // multiply, so the normalised weights sum to one (exact for one dominant key)
+  uint32_t pw[8];
+  float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bf16x2 pr;
+    pr[0] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i], c, -s.m)));
+    pr[1] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i + 1], c, -s.m)));
+    pw[i] = __builtin_bit_cast(uint32_t, pr);
+    ps0 += __uint_as_float(pw[i] << 16);
+    ps1 += __uint_as_float(pw[i] & 0xFFFF0000u);
+  }
+  s.lsum += ps0 + ps1;
+  const u32x4 plo = {pw[0], pw[1], pw[2], pw[3]}, phi = {pw[4], pw[5], pw[6], pw[7]};
+  const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, plo), __builtin_bit_cast(bf16x8, phi)};
+  // O^T += V^T P^T; B slot t of pb[ks] is key 16ks + 8(t/4) + 4g + t%4, and the two
+  // transposing reads give this lane's d the same keys
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 wv = {vfr[dt][ks][0].x, vfr[dt][ks][0].y, vfr[dt][ks][1].x, vfr[dt][ks][1].y};
+      s.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), pb[ks],
+                                                          s.acc[dt], 0, 0, 0);
+    }
+  }
+}
 
 template <int D>
 __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
-  constexpr int KS = D / 16;                  // MFMA k-steps over d (S^T)
-  constexpr int DT = D / 32;                  // 32-wide d tiles (O^T)
-  constexpr int CH = D / 8;                   // 16-byte chunks per token row
-  constexpr int ROWB = D * 2;                 // bytes per token row
-  constexpr int TILE = 32 * ROWB;             // bytes per 32-token K (or V) tile
-  constexpr int LOADS = TILE / (128 * 16);    // 16-byte loads per thread per operand
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILE];
+  using L = AttnLane<D>;
+  constexpr int KS = L::KS, DT = L::DT, ROWB = L::ROWB, TILE = L::TILE, LOADS = L::LOADS;
+  // Double-buffered K and V tiles as four separate LDS objects, so the compiler can tell
+  // that reading one buffer does not alias the in-flight copy into the other.
+  __shared__ __attribute__((aligned(1024))) unsigned char k_buf0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_buf0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_buf1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_buf1[TILE];
+  __shared__ int2 tile_s[2 * kListSeg];       // (first token, valid tokens) per 32-token tile
 
   // head-major work order, consecutive work items on one XCD (workgroups are dealt
   // round-robin over the 8 XCDs)
@@ -149,7 +284,8 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   const int work = xcd * per + min(xcd, rem) + slot;
   const int bh = work / a.n_qb, r = work - bh * a.n_qb;
 
-  const int tid = threadIdx.x, w = tid / 64, l = tid % 64, j = l % 32, g = l / 32;
+  const int tid = threadIdx.x, l = tid % 64, j = l % 32, g = l / 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const BlockGeom geo{a.tpf, a.bs, a.n_bpf};
   const int q_start = geo.start(r), q_len = geo.len(r);
   const int nq = min(max(q_len - 32 * w, 0), 32);
@@ -158,31 +294,25 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   const __bf16* Kg = static_cast<const __bf16*>(a.k) + static_cast<size_t>(bh) * a.lk * D;
   const __bf16* Vg = static_cast<const __bf16*>(a.v) + static_cast<size_t>(bh) * a.lk * D;
 
-  // Q^T fragments: lane (query j, half g) holds d = 16s + 8g .. +7 of its row
-  bf16x8 qf[KS];
+  L s;
   {
     const int qrow = q_start + min(32 * w + j, q_len - 1);
     const __bf16* qp = Qg + static_cast<size_t>(qrow) * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    for (int st = 0; st < KS; ++st) s.qf[st] = *reinterpret_cast<const bf16x8*>(qp + 16 * st);
   }
-
-  f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.f;
-  float m = -1e30f, lsum = 0.f;   // max in use (scaled log2 units) and partial row sum
+    for (int v = 0; v < 16; ++v) s.acc[dt][v] = 0.f;
+  s.m = -1e30f;
+  s.lsum = 0.f;
   const float c = a.scale_log2;
-
-  // per-lane byte offsets inside a tile, independent of the tile
-  int k_off[KS];                              // K A-operand: row j, chunk 2s+g (swizzled)
 #pragma unroll
-  for (int s = 0; s < KS; ++s) k_off[s] = j * ROWB + (((2 * s + g) ^ (j & (CH - 1))) * 16);
+  for (int st = 0; st < KS; ++st) s.k_off[st] = j * ROWB + (((2 * st + g) ^ k_swz<D>(j)) * 16);
   // V^T A-operand via transposing reads: this lane supplies row 16ks + 8h + 4g + (l%16)/4,
   // columns 32dt + 16((l/16)%2) + 4(l%4) .. +3
   const int grp = l / 16, i16 = l % 16;
-  int v_off[DT][2][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -191,125 +321,76 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
       for (int h = 0; h < 2; ++h) {
         const int key = 16 * ks + 8 * h + 4 * g + i16 / 4;
         const int d = 32 * dt + 16 * (grp % 2) + 4 * (i16 % 4);
-        v_off[dt][ks][h] = key * ROWB + (((d / 8) ^ (key & (CH - 1))) * 16) + (d % 8) * 2;
+        s.v_off[dt][ks][h] = key * ROWB + (((d / 8) ^ v_swz<D>(key)) * 16) + (d % 8) * 2;
       }
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int off = (i * 2 + w) * 1024 + l * 16;
+    const int row = off / ROWB, pc = (off % ROWB) / 16;   // physical chunk
+    s.cp_row[i] = row;
+    s.cp_koff[i] = row * ROWB + (pc ^ k_swz<D>(row)) * 16;
+    s.cp_voff[i] = row * ROWB + (pc ^ v_swz<D>(row)) * 16;
+  }
+
+  auto tile = [&](int t) {                    // wave-uniform (first token, valid tokens)
+    const int2 v = tile_s[t];
+    return make_int2(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y));
+  };
 
   const int* bl = a.blocks + static_cast<size_t>(work) * a.W_b;
-  auto ok = [&](int e) {
-    const int gg = bl[e];
-    return gg >= 0 && gg < a.n_kb;
-  };
-
-  auto issue = [&](int buf, int tok0, int nv) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int base = (i * 2 + w) * 1024;    // wave-uniform LDS offset
-      const int off = base + l * 16;
-      const int row = off / ROWB;
-      const int cc = ((off % ROWB) / 16) ^ (row & (CH - 1));
-      const size_t src = static_cast<size_t>(tok0 + min(row, nv - 1)) * D + cc * 8;
-      __builtin_amdgcn_global_load_lds(Kg + src, (__attribute__((address_space(3))) void*)(&smem[buf][0][base]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vg + src, (__attribute__((address_space(3))) void*)(&smem[buf][1][base]), 16, 0, 0);
+  for (int seg0 = 0; seg0 < a.W_b; seg0 += kListSeg) {
+    const int nseg = min(kListSeg, a.W_b - seg0);
+    const int nt = 2 * nseg;
+    __syncthreads();                          // previous segment fully consumed
+    for (int i = tid; i < nseg; i += 128) {
+      const int gg = bl[seg0 + i];
+      int2 t0 = make_int2(0, 0), t1 = make_int2(0, 0);
+      if (gg >= 0 && gg < a.n_kb) {
+        const int st = geo.start(gg), len = geo.len(gg);
+        t0 = make_int2(st, min(32, len));
+        if (len > 32) t1 = make_int2(st + 32, len - 32);
+      }
+      tile_s[2 * i] = t0;
+      tile_s[2 * i + 1] = t1;
     }
-  };
-
-  int n = 0, p = 0;
-  while (n < a.W_b && !ok(n)) ++n;
-  if (n < a.W_b) {
-    const int g0 = bl[n];
-    issue(0, geo.start(g0), min(32, geo.len(g0)));
-  }
-  int buf = 0;
-  while (n < a.W_b) {
-    const int gc = bl[n];
-    const int kl = geo.len(gc);
-    const int nv = min(32, kl - 32 * p);
-    int n2 = n, p2 = p + 1;
-    if (32 * p2 >= kl) {
-      p2 = 0;
-      ++n2;
-      while (n2 < a.W_b && !ok(n2)) ++n2;
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (n2 < a.W_b) {
-      const int gn = bl[n2];
-      issue(buf ^ 1, geo.start(gn) + 32 * p2, min(32, geo.len(gn) - 32 * p2));
-    }
 
-    if (nq > 0) {
-      const lds_u8* Kt = (const lds_u8*)(&smem[buf][0][0]);
-      const lds_u8* Vt = (const lds_u8*)(&smem[buf][1][0]);
-      f32x16 sacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>((const unsigned char*)(Kt + k_off[s]));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
-      }
-      // sacc[v] = S^T[key 8(v/4) + 4g + v%4][query j]; scale > 0, so the max of the raw
-      // scores gives the max of the scaled ones
-      if (nv < 32) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (8 * (v / 4) + 4 * g + (v % 4) >= nv) sacc[v] = -INFINITY;
-      }
-      float mt = sacc[0];
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
-      const bool grow = mt > m + kRescaleSlack;
-      if (__any(grow)) {
-        const float mn = grow ? mt : m;
-        const float corr = fast_exp2(m - mn);
-        m = mn;
-        lsum *= corr;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[dt][v] *= corr;
-      }
-      // P^T as bf16 pairs; the row sum takes the same rounded weights the matrix cores
-      // multiply, so the normalised weights sum to one (exact for a single dominant key)
-      uint32_t pw[8];
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bf16x2 pr;
-        pr[0] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i], c, -m)));
-        pr[1] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i + 1], c, -m)));
-        pw[i] = __builtin_bit_cast(uint32_t, pr);
-        ps0 += __uint_as_float(pw[i] << 16);
-        ps1 += __uint_as_float(pw[i] & 0xFFFF0000u);
-      }
-      lsum += ps0 + ps1;
-      bf16x8 pb[2];
-      {
-        const u32x4 lo = {pw[0], pw[1], pw[2], pw[3]}, hi = {pw[4], pw[5], pw[6], pw[7]};
-        pb[0] = __builtin_bit_cast(bf16x8, lo);
-        pb[1] = __builtin_bit_cast(bf16x8, hi);
-      }
-      // O^T += V^T P^T; B slot t of pb[ks] is key 16ks + 8(t/4) + 4g + t%4, and the two
-      // transposing reads give this lane's d the same keys
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint2 lo = ds_read_tr16(Vt + v_off[dt][ks][0]);
-          const uint2 hi = ds_read_tr16(Vt + v_off[dt][ks][1]);
-          const uint32_t wv[4] = {lo.x, lo.y, hi.x, hi.y};
-          const bf16x8 va = __builtin_bit_cast(bf16x8, wv);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], acc[dt], 0, 0, 0);
-        }
-      }
+    int t = 0;
+    while (t < nt && tile(t).y == 0) ++t;
+    if (t < nt) {
+      const int2 tt = tile(t);
+      issue_tile<D>(k_buf0, v_buf0, Kg, Vg, tt.x, tt.y, s, w);
     }
-    buf ^= 1;
-    n = n2;
-    p = p2;
+    // two tiles per iteration so each LDS buffer index is a compile-time constant
+    while (t < nt) {
+      int t2 = t + 1;
+      while (t2 < nt && tile(t2).y == 0) ++t2;
+      const int nv0 = tile(t).y;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t2 < nt) {
+        const int2 tt = tile(t2);
+        issue_tile<D>(k_buf1, v_buf1, Kg, Vg, tt.x, tt.y, s, w);
+      }
+      if (nq > 0) tile_compute<D>(k_buf0, v_buf0, nv0, g, c, s);
+      t = t2;
+      if (t >= nt) break;
+
+      t2 = t + 1;
+      while (t2 < nt && tile(t2).y == 0) ++t2;
+      const int nv1 = tile(t).y;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t2 < nt) {
+        const int2 tt = tile(t2);
+        issue_tile<D>(k_buf0, v_buf0, Kg, Vg, tt.x, tt.y, s, w);
+      }
+      if (nq > 0) tile_compute<D>(k_buf1, v_buf1, nv1, g, c, s);
+      t = t2;
+    }
   }
 
-  const float lt = lsum + __shfl_xor(lsum, 32, 64);
+  const float lt = s.lsum + __shfl_xor(s.lsum, 32, 64);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (j < nq) {
     __bf16* op = static_cast<__bf16*>(a.o) + (static_cast<size_t>(bh) * a.lq + q_start + 32 * w + j) * D;
@@ -320,7 +401,7 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
         typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
         bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = static_cast<__bf16>(acc[dt][4 * v4 + e] * inv);
+        for (int e = 0; e < 4; ++e) ov[e] = static_cast<__bf16>(s.acc[dt][4 * v4 + e] * inv);
         *reinterpret_cast<bf16x4*>(op + 32 * dt + 8 * v4 + 4 * g) = ov;
       }
     }
