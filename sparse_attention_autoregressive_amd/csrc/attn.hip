@@ -117,6 +117,8 @@ typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): inside each group of 16 lanes, lane
 // c receives element (c % 4) of the 8-byte words addressed by lanes c/4, 4 + c/4,
@@ -154,114 +156,117 @@ struct AttnLane {
   static constexpr int LOADS = TILE / (128 * 16);
   bf16x8 qf[KS];                              // Q^T fragments (query j, d 16s + 8g ..)
   f32x16 acc[DT];                             // O^T accumulators (query j)
-  float m, lsum;                              // max in use (scaled log2 units), row sum
+  f32x4 lsum;                                 // row sum of query j (all four entries)
+  bf16x8 sum_sel;                             // 0/1 selector operand of the row-sum MFMA
+  float m;                                    // max in use (scaled log2 units)
   int k_off[KS];                              // K A-operand byte offsets in a tile
-  int v_off[DT][2][2];                        // V^T transposing-read byte offsets
-  int cp_row[LOADS];                          // global -> LDS copy: tile row of this lane
-  int cp_koff[LOADS], cp_voff[LOADS];         // ... and its byte offset in a full tile
+  int v_off[DT];                              // V^T transposing-read byte offsets (keys 0..3)
+  int cp_koff[LOADS], cp_voff[LOADS];         // global -> LDS copy: tile byte offset of slot l
 };
 
-// Copies the 32-token K and V tiles starting at token tok0 (nv valid rows; rows past nv
-// repeat the last valid one and are masked later) from global memory straight into
-// LDS. Each wave fills 1 KB pieces 2i + w of each tile; the lane writes its 16-byte slot
-// and fetches the chunk that the tile's swizzle maps there.
+// K and V of one (b, h) are read through buffer resources: the tile's first byte goes in
+// a scalar offset and each lane adds a fixed 32-bit offset, so the copies need no vector
+// address arithmetic. Reads past the resource's size return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// Copies the 32-token K and V tiles starting at token tok0 from global memory straight
+// into LDS. Each wave fills 1 KB pieces 2i + w of each tile; the lane writes its 16-byte
+// slot and fetches the chunk that the tile's swizzle maps there. Rows past the tile's
+// valid tokens are copied as they are (tokens of the next block, or zeros past the end of
+// the buffer): their scores are masked, so they meet zero weights.
 template <int D>
-__device__ __forceinline__ void issue_tile(unsigned char* k_lds, unsigned char* v_lds,
-                                           const __bf16* Kg, const __bf16* Vg, int tok0, int nv,
+__device__ __forceinline__ void issue_tile(lds_u8* k_lds, lds_u8* v_lds, rsrc_t kr, rsrc_t vr, int tok0,
                                            const AttnLane<D>& s, int w) {
-  constexpr int ROWB = AttnLane<D>::ROWB;
-  const char* kb = reinterpret_cast<const char*>(Kg + static_cast<size_t>(tok0) * D);
-  const char* vb = reinterpret_cast<const char*>(Vg + static_cast<size_t>(tok0) * D);
-  if (nv == 32) {
+  const int base = __builtin_amdgcn_readfirstlane(tok0 * AttnLane<D>::ROWB);
 #pragma unroll
-    for (int i = 0; i < AttnLane<D>::LOADS; ++i) {
-      const int base = (i * 2 + w) * 1024;    // wave-uniform LDS offset
-      __builtin_amdgcn_global_load_lds(kb + s.cp_koff[i], (__attribute__((address_space(3))) void*)(k_lds + base), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + s.cp_voff[i], (__attribute__((address_space(3))) void*)(v_lds + base), 16, 0, 0);
-    }
-  } else {                                    // short tile: clamp rows to the last valid one
-#pragma unroll
-    for (int i = 0; i < AttnLane<D>::LOADS; ++i) {
-      const int base = (i * 2 + w) * 1024;
-      const int dr = (min(s.cp_row[i], nv - 1) - s.cp_row[i]) * ROWB;
-      __builtin_amdgcn_global_load_lds(kb + s.cp_koff[i] + dr, (__attribute__((address_space(3))) void*)(k_lds + base), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + s.cp_voff[i] + dr, (__attribute__((address_space(3))) void*)(v_lds + base), 16, 0, 0);
-    }
+  for (int i = 0; i < AttnLane<D>::LOADS; ++i) {
+    const int piece = (i * 2 + w) * 1024;     // wave-uniform LDS offset
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(k_lds + piece), 16, s.cp_koff[i], base, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(v_lds + piece), 16, s.cp_voff[i], base, 0, 0);
   }
 }
 
 // One 32-token tile of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 template <int D>
-__device__ __forceinline__ void tile_compute(const unsigned char* Kt_, const unsigned char* Vt_,
-                                             int nv, int g, float c, AttnLane<D>& s) {
-  constexpr int KS = AttnLane<D>::KS, DT = AttnLane<D>::DT;
-  const lds_u8* Kt = (const lds_u8*)Kt_;
-  const lds_u8* Vt = (const lds_u8*)Vt_;
-  bf16x8 kf[KS];
-#pragma unroll
-  for (int st = 0; st < KS; ++st) kf[st] = *reinterpret_cast<const bf16x8*>((const unsigned char*)(Kt + s.k_off[st]));
+__device__ __forceinline__ void tile_compute(const lds_u8* Kt, const lds_u8* Vt, int nv, int g, float c,
+                                             AttnLane<D>& s) {
+  constexpr int KS = AttnLane<D>::KS, DT = AttnLane<D>::DT, ROWB = AttnLane<D>::ROWB;
+  typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
   f32x16 sacc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
-  for (int st = 0; st < KS; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], s.qf[st], sacc, 0, 0, 0);
-  // V^T fragments, in flight while the softmax runs
-  uint2 vfr[DT][2][2];
+  for (int st = 0; st < KS; ++st) {
+    const bf16x8 kf = *reinterpret_cast<lds_bf16x8*>(Kt + s.k_off[st]);
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, s.qf[st], sacc, 0, 0, 0);
+  }
+  // V^T fragments, in flight while the softmax runs; rows 16ks + 8h of the lane's column
+  bf16x8 vf[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) vfr[dt][ks][h] = ds_read_tr16(Vt + s.v_off[dt][ks][h]);
-  // sacc[v] = S^T[key 8(v/4) + 4g + v%4][query j]; scale > 0, so the max of the raw
-  // scores gives the max of the scaled ones
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint2 lo = ds_read_tr16(Vt + s.v_off[dt] + 16 * ks * ROWB);
+      const uint2 hi = ds_read_tr16(Vt + s.v_off[dt] + (16 * ks + 8) * ROWB);
+      const u32x4 wv = {lo.x, lo.y, hi.x, hi.y};
+      vf[dt][ks] = __builtin_bit_cast(bf16x8, wv);
+    }
+  // sacc[v] = S^T[key 8(v/4) + 4g + v%4][query j]. Short tiles (rare) mask their tail
+  // keys; the empty asm keeps the compiler from turning the branch into selects that
+  // would run on every tile.
   if (nv < 32) {
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (8 * (v / 4) + 4 * g + (v % 4) >= nv) sacc[v] = -INFINITY;
   }
+  // scale > 0, so the max of the raw scores gives the max of the scaled ones; lanes j and
+  // j + 32 hold the two key halves of query j
   float mt = sacc[0];
 #pragma unroll
   for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * c;
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+  mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
   const bool grow = mt > s.m + kRescaleSlack;
   if (__any(grow)) {
     const float mn = grow ? mt : s.m;
     const float corr = fast_exp2(s.m - mn);
     s.m = mn;
-    s.lsum *= corr;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s.lsum[v] *= corr;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s.acc[dt][v] *= corr;
   }
-  // P^T as bf16 pairs; the row sum takes the same rounded weights the matrix cores
-  // multiply, so the normalised weights sum to one (exact for one dominant key)
+  // P^T as bf16 pairs; B slot t of pb[ks] is key 16ks + 8(t/4) + 4g + t%4
   uint32_t pw[8];
-  float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     bf16x2 pr;
     pr[0] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i], c, -s.m)));
     pr[1] = static_cast<__bf16>(fast_exp2(fmaf(sacc[2 * i + 1], c, -s.m)));
     pw[i] = __builtin_bit_cast(uint32_t, pr);
-    ps0 += __uint_as_float(pw[i] << 16);
-    ps1 += __uint_as_float(pw[i] & 0xFFFF0000u);
   }
-  s.lsum += ps0 + ps1;
   const u32x4 plo = {pw[0], pw[1], pw[2], pw[3]}, phi = {pw[4], pw[5], pw[6], pw[7]};
   const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, plo), __builtin_bit_cast(bf16x8, phi)};
-  // O^T += V^T P^T; B slot t of pb[ks] is key 16ks + 8(t/4) + 4g + t%4, and the two
-  // transposing reads give this lane's d the same keys
+  // O^T += V^T P^T; the two transposing reads give this lane's d the same keys
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 wv = {vfr[dt][ks][0].x, vfr[dt][ks][0].y, vfr[dt][ks][1].x, vfr[dt][ks][1].y};
-      s.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv), pb[ks],
-                                                          s.acc[dt], 0, 0, 0);
-    }
-  }
+    for (int ks = 0; ks < 2; ++ks)
+      s.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt][ks], pb[ks], s.acc[dt], 0, 0, 0);
+  // Row sums on the matrix cores, from the same rounded weights the PV product uses (so
+  // the normalised weights sum to one). Read as a 16x16x32 product, the B operand pb holds
+  // in lane l column l%16 with the 8 keys of lane group l/16; groups 0 and 2 belong to
+  // query l%16, groups 1 and 3 to query 16 + l%16. The selector has ones in rows
+  // {0-3, 8-11} for groups {0, 2} and in rows {4-7, 12-15} for groups {1, 3}, so the rows
+  // lane l receives (4(l/16) .. +3 of column l%16) all hold the sum of query l%32.
+  s.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.sum_sel, pb[0], s.lsum, 0, 0, 0);
+  s.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.sum_sel, pb[1], s.lsum, 0, 0, 0);
 }
 
 template <int D>
@@ -275,6 +280,10 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_buf1[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v_buf1[TILE];
   __shared__ int2 tile_s[2 * kListSeg];       // (first token, valid tokens) per 32-token tile
+  lds_u8* const kb0 = (lds_u8*)k_buf0;
+  lds_u8* const vb0 = (lds_u8*)v_buf0;
+  lds_u8* const kb1 = (lds_u8*)k_buf1;
+  lds_u8* const vb1 = (lds_u8*)v_buf1;
 
   // head-major work order, consecutive work items on one XCD (workgroups are dealt
   // round-robin over the 8 XCDs)
@@ -291,8 +300,9 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   const int nq = min(max(q_len - 32 * w, 0), 32);
 
   const __bf16* Qg = static_cast<const __bf16*>(a.q) + static_cast<size_t>(bh) * a.lq * D;
-  const __bf16* Kg = static_cast<const __bf16*>(a.k) + static_cast<size_t>(bh) * a.lk * D;
-  const __bf16* Vg = static_cast<const __bf16*>(a.v) + static_cast<size_t>(bh) * a.lk * D;
+  const uint32_t kv_bytes = static_cast<uint32_t>(a.lk) * ROWB;
+  const rsrc_t kr = make_rsrc(static_cast<const __bf16*>(a.k) + static_cast<size_t>(bh) * a.lk * D, kv_bytes);
+  const rsrc_t vr = make_rsrc(static_cast<const __bf16*>(a.v) + static_cast<size_t>(bh) * a.lk * D, kv_bytes);
 
   L s;
   {
@@ -306,28 +316,32 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) s.acc[dt][v] = 0.f;
   s.m = -1e30f;
-  s.lsum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s.lsum[v] = 0.f;
+  {
+    const bool rows_a = ((l % 16) & 4) == 0;            // selector rows 0-3 and 8-11
+    const bool grp_a = ((l / 16) & 1) == 0;             // key groups 0 and 2
+    const __bf16 one = static_cast<__bf16>(rows_a == grp_a ? 1.0f : 0.0f);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s.sum_sel[t] = one;
+  }
   const float c = a.scale_log2;
 #pragma unroll
   for (int st = 0; st < KS; ++st) s.k_off[st] = j * ROWB + (((2 * st + g) ^ k_swz<D>(j)) * 16);
   // V^T A-operand via transposing reads: this lane supplies row 16ks + 8h + 4g + (l%16)/4,
-  // columns 32dt + 16((l/16)%2) + 4(l%4) .. +3
+  // columns 32dt + 16((l/16)%2) + 4(l%4) .. +3. The swizzle depends only on the row's low
+  // bits, which 16ks + 8h leaves alone, so one offset per dt serves all four reads.
   const int grp = l / 16, i16 = l % 16;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = 16 * ks + 8 * h + 4 * g + i16 / 4;
-        const int d = 32 * dt + 16 * (grp % 2) + 4 * (i16 % 4);
-        s.v_off[dt][ks][h] = key * ROWB + (((d / 8) ^ v_swz<D>(key)) * 16) + (d % 8) * 2;
-      }
+  for (int dt = 0; dt < DT; ++dt) {
+    const int key = 4 * g + i16 / 4;
+    const int d = 32 * dt + 16 * (grp % 2) + 4 * (i16 % 4);
+    s.v_off[dt] = key * ROWB + (((d / 8) ^ v_swz<D>(key)) * 16) + (d % 8) * 2;
+  }
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int off = (i * 2 + w) * 1024 + l * 16;
     const int row = off / ROWB, pc = (off % ROWB) / 16;   // physical chunk
-    s.cp_row[i] = row;
     s.cp_koff[i] = row * ROWB + (pc ^ k_swz<D>(row)) * 16;
     s.cp_voff[i] = row * ROWB + (pc ^ v_swz<D>(row)) * 16;
   }
@@ -359,7 +373,7 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
     while (t < nt && tile(t).y == 0) ++t;
     if (t < nt) {
       const int2 tt = tile(t);
-      issue_tile<D>(k_buf0, v_buf0, Kg, Vg, tt.x, tt.y, s, w);
+      issue_tile<D>(kb0, vb0, kr, vr, tt.x, s, w);
     }
     // two tiles per iteration so each LDS buffer index is a compile-time constant
     while (t < nt) {
@@ -370,9 +384,9 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
       __syncthreads();
       if (t2 < nt) {
         const int2 tt = tile(t2);
-        issue_tile<D>(k_buf1, v_buf1, Kg, Vg, tt.x, tt.y, s, w);
+        issue_tile<D>(kb1, vb1, kr, vr, tt.x, s, w);
       }
-      if (nq > 0) tile_compute<D>(k_buf0, v_buf0, nv0, g, c, s);
+      if (nq > 0) tile_compute<D>(kb0, vb0, nv0, g, c, s);
       t = t2;
       if (t >= nt) break;
 
@@ -383,14 +397,14 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
       __syncthreads();
       if (t2 < nt) {
         const int2 tt = tile(t2);
-        issue_tile<D>(k_buf0, v_buf0, Kg, Vg, tt.x, tt.y, s, w);
+        issue_tile<D>(kb0, vb0, kr, vr, tt.x, s, w);
       }
-      if (nq > 0) tile_compute<D>(k_buf1, v_buf1, nv1, g, c, s);
+      if (nq > 0) tile_compute<D>(kb1, vb1, nv1, g, c, s);
       t = t2;
     }
   }
 
-  const float lt = s.lsum + __shfl_xor(s.lsum, 32, 64);
+  const float lt = s.lsum[0];                 // both key halves already summed
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (j < nq) {
     __bf16* op = static_cast<__bf16*>(a.o) + (static_cast<size_t>(bh) * a.lq + q_start + 32 * w + j) * D;
