@@ -32,8 +32,9 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 import sparse_attention_autoregressive_amd as lf  # noqa: E402
-from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, Workspace, attend, pool_k,  # noqa: E402
-                                                          pool_q, select_blocks, select_frames)
+from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, SweepWorkspace, Workspace,  # noqa: E402
+                                                          attend, plan_sweep, pool_k, pool_q, select_blocks,
+                                                          select_frames, sweep_layer)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
@@ -72,7 +73,7 @@ def pool_bytes(w, n_frames, with_frames):
     return rd + wr
 
 
-def run_cpu_baseline(w, heads: int, min_s: float):
+def run_cpu_baseline(w, k_b: int, heads: int, min_s: float):
     """The CPU oracle (numpy fp64) on the first `heads` heads of one layer: pool, select
     and attend, repeated until at least `min_s` seconds have passed. Returns
     (dense-equiv TFLOP/s, seconds, repeats, dense flops of one repeat)."""
@@ -86,7 +87,7 @@ def run_cpu_baseline(w, heads: int, min_s: float):
     while reps == 0 or dt < min_s:
         t0 = time.perf_counter()
         out = oracle.hsa(q64, k64, v64, tpf=ws.tpf, bs=ws.bs, n_kframes=ws.n_kframes, mem=ws.mem,
-                         forced=ws.forced, k_f=ws.k_f, k_b=w.k_b, scale=ws.scale)
+                         forced=ws.forced, k_f=ws.k_f, k_b=k_b, scale=ws.scale)
         dt += time.perf_counter() - t0
         reps += 1
     dense, _ = flops_of(ws, out["blocks"])
@@ -107,7 +108,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="480p_chunk7of7", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--workload", default="480p_chunk2of7", choices=sorted(synth.WORKLOADS) + [synth.SWEEP.name])
     ap.add_argument("--layers", type=int, default=4, help="independent input sets cycled per step")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-min-s", type=float, default=10.0, help="repeat the CPU sample for at least this long")
@@ -119,6 +120,8 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == synth.SWEEP.name:
+        return bench_sweep(args)
     dev = torch.device("cuda")
     w = synth.WORKLOADS[args.workload]
     g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
@@ -209,7 +212,7 @@ def main():
     cpu = None
     if args.cpu_heads > 0:
         print(f"[bench] CPU oracle on {args.cpu_heads} heads", file=sys.stderr, flush=True)
-        cpu_tflops, cpu_s, reps, cpu_dense = run_cpu_baseline(w, args.cpu_heads, args.cpu_min_s)
+        cpu_tflops, cpu_s, reps, cpu_dense = run_cpu_baseline(w, k_b, args.cpu_heads, args.cpu_min_s)
         cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
                "sample": f"{w.name}, heads 0..{args.cpu_heads - 1} of {w.H}: pool + select + attention "
                          f"in numpy fp64, {reps} repeats ({cpu_dense:.3e} dense-equiv FLOP each) "
@@ -245,6 +248,116 @@ def main():
         "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+STAGES = ["pool_q", "pool_k", "select_frames", "select_blocks", "attn"]
+
+
+def bench_sweep(args):
+    """The full Chunk-Aware Growth schedule of one denoising step of a 5-s 480p clip:
+    30 layers x 7 chunks (chunk 1 dense). One step = the whole schedule; inputs of all 30
+    layers (independent, drawn on the device) are resident before timing."""
+    s = synth.SWEEP
+    dev = torch.device("cuda")
+    g = lf.Geom(s.B, s.H, s.d, s.tpf, s.bs)
+    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5)
+    sw = SweepWorkspace(sp, torch.bfloat16, dev)
+    pools = [s.chunk(i).q_pool for i in range(1, s.n_chunks + 1)]
+    n_layers = s.n_layers
+    print(f"[bench] generating {n_layers} layers for {s.name}", file=sys.stderr, flush=True)
+    layers = [synth.make_on_device(s.B, s.H, s.n_frames, s.n_frames, s.tpf, s.bs, s.d, s.dtype, s.seed(li),
+                                   dev, pools) for li in range(n_layers)]
+    o = torch.empty_like(layers[0][0])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # untimed pass: every (layer, chunk) block list, for the active FLOP count
+    f_dense, f_active = 0.0, 0.0
+    for li, (q, k, v) in enumerate(layers):
+        sweep_layer(sw, q, k, v, o)
+        torch.cuda.synchronize()
+        for i in range(1, s.n_chunks + 1):
+            w = s.chunk(i, li)
+            blocks = (sw.full[i] if sp.dense(i) else sw.chunks[i - 1].blocks).cpu().numpy()
+            fd, fa = flops_of(w, blocks)
+            f_dense += fd
+            f_active += fa
+
+    def run(events=None):
+        for q, k, v in layers:
+            mark = None
+            if events is not None:
+                def mark(i, stage):
+                    ev = torch.cuda.Event(enable_timing=True)
+                    ev.record(stream)
+                    events.append((i, stage, ev))
+            sweep_layer(sw, q, k, v, o, mark)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} sweeps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # per-stage breakdown from one extra evented sweep (events add host overhead)
+    events = []
+    run(events)
+    torch.cuda.synchronize()
+    stage_us = {st: 0.0 for st in STAGES}
+    chunk_us = [0.0] * s.n_chunks
+    for (i, st, ev), (_, _, nxt) in zip(events, events[1:]):
+        if st == "end":
+            continue
+        dt = ev.elapsed_time(nxt) * 1e3
+        stage_us[st] += dt
+        chunk_us[i - 1] += dt
+    t_attn = stage_us["attn"] * 1e-6
+    attn_tflops = f_active / t_attn / 1e12
+    cpu = None
+    if args.cpu_heads > 0:
+        w7 = s.chunk(s.n_chunks, 0)
+        k_b7 = sp.chunks[-1].k_b
+        print(f"[bench] CPU oracle on {args.cpu_heads} heads of {w7.name}", file=sys.stderr, flush=True)
+        cpu_tflops, cpu_s, reps, cpu_dense = run_cpu_baseline(w7, k_b7, args.cpu_heads, args.cpu_min_s)
+        cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{w7.name} (chunk 7, layer 0), heads 0..{args.cpu_heads - 1}: pool + select + "
+                         f"attention in numpy fp64, {reps} repeats ({cpu_dense:.3e} dense-equiv FLOP each) "
+                         f"in {cpu_s:.1f} s",
+               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or platform.machine()}
+    line = {
+        "metric": METRIC,
+        "value": f_dense / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded planted-relevance Q/K/V drawn on the device; no model weights)",
+        "config": {"workload": s.name, "layers": n_layers, "chunks": s.n_chunks, "H": s.H, "d": s.d,
+                   "tokens_per_frame": s.tpf, "block_size": s.bs, "k_f": s.k_f,
+                   "cag_s": [round(x, 6) for x in sp.s], "cag_beta": sp.beta,
+                   "k_b": [c.k_b for c in sp.chunks], "W_b": [c.W_b for c in sp.chunks]},
+        "mfma_pct_peak_active": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
+        "select_overhead_pct": 100.0 * (stage_us["select_frames"] + stage_us["select_blocks"]) / stage_us["attn"],
+        "pool_select_pct_of_attn": 100.0 * (sum(stage_us.values()) - stage_us["attn"]) / stage_us["attn"],
+        "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
+        "stage_us_per_sweep": {k: round(v, 1) for k, v in stage_us.items()},
+        "chunk_us_per_sweep": [round(x, 1) for x in chunk_us],
+        "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": attn_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

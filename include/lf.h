@@ -26,7 +26,12 @@
  *     n_bpf = ceil(tpf/bs) blocks, the last one possibly shorter; the global block id of
  *     block j of frame f is f*n_bpf + j. Queries use the same rule on the chunk's own
  *     frames (query block r = frame r/n_bpf, block r%n_bpf).
- *   - Tensors are [B, H, tokens, d]: batch, head, token, channel.
+ *   - Token tensors (x, q, k, v, o) are [B, H, tokens, d]: batch, head, token, channel,
+ *     with each (b, h) slice contiguous. g.head_stride is the distance in tokens between
+ *     consecutive (b, h) slices: 0 means packed (the tensor's own token count); a larger
+ *     value addresses a prefix or a window of a bigger allocation, such as an
+ *     autoregressive KV cache sized for the whole video (all token tensors of one call
+ *     then share that stride). Pooled tensors and id lists are always packed.
  */
 #ifndef LF_H
 #define LF_H
@@ -37,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LF_ABI_VERSION 1
+#define LF_ABI_VERSION 2
 
 typedef enum {
   LF_OK = 0,
@@ -49,9 +54,11 @@ typedef enum {
 
 typedef enum { LF_FP32 = 0, LF_BF16 = 1 } lf_dtype;
 
-/* B batch, H heads, d head dim, tokens_per_frame (tpf), block_size (bs). */
+/* B batch, H heads, d head dim, tokens_per_frame (tpf), block_size (bs), head_stride
+ * (tokens between (b, h) slices of the token tensors; 0 = packed). */
 typedef struct {
   int32_t B, H, d, tokens_per_frame, block_size;
+  int32_t head_stride;
 } lf_geom;
 
 /* Message for the last failing call on the calling thread ("" if none). The pointer
@@ -95,13 +102,16 @@ lf_status lf_block_budget(double s, int32_t n_kblocks, int32_t W_f, int32_t n_bp
 
 /* ---------------------------------------------------------------------------------
  * lf_pool -- [S2] token compression by mean pooling.
- * x: [B, H, n_frames*tpf, d] in dtype dt (LF_BF16 or LF_FP32).
+ * x: [B, H, n_frames*tpf, d] in dtype dt (LF_BF16 or LF_FP32); with a nonzero
+ *   g.head_stride the (b, h) slice starts at x + (b*H + h)*head_stride*d
+ *   (head_stride >= n_frames*tpf).
  * blk_out: [B, H, n_frames*n_bpf, d] fp32, the mean of each block's tokens (q~ for the
  *   chunk's queries, k~ for keys), divided by the block's true token count.
  * frm_out: [B, H, n_frames, d] fp32, the mean of each frame's tpf tokens (k^), or NULL
  *   to skip (e.g. when pooling queries). Frame means are formed from the fp32 block
  *   means weighted by their token counts.
- * Limits: d in {64, 128}; 1 <= bs <= tpf; tpf <= 65536; n_frames >= 1; B, H >= 1.
+ * Limits: d in {64, 128}; 1 <= bs <= tpf; tpf <= 65536; n_frames >= 1; B, H >= 1;
+ *   head_stride = 0 or >= n_frames*tpf.
  * Errors: LF_ERR_INVALID_ARG (NULL/unaligned pointers, bad sizes), LF_ERR_UNSUPPORTED
  *   (d or dtype), LF_ERR_HIP (launch).
  * ------------------------------------------------------------------------------- */
@@ -151,6 +161,7 @@ lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, in
  *   o_t = sum_u softmax_u(scale * <q_t, k_u>) v_u   (softmax over the listed tokens).
  * With every block listed this is dense attention (CAG's first chunk).
  * q, o: [B, H, n_qframes*tpf, d]; k, v: [B, H, n_kframes*tpf, d]; all in dtype dt.
+ *   A nonzero g.head_stride (>= both token counts) applies to all four tensors.
  * blocks: [B, H, n_qb, W_b] int32 device array, n_qb = n_qframes*n_bpf; ids should be
  *   unique (a repeated id is counted twice); ids outside [0, n_kframes*n_bpf) are
  *   skipped. A row with no valid id produces zeros.

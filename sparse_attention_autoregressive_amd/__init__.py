@@ -30,14 +30,20 @@ def library_path() -> str:
 
 
 class Geom(ctypes.Structure):
-    """lf_geom: batch, heads, head dim, tokens per frame, tokens per block."""
+    """lf_geom: batch, heads, head dim, tokens per frame, tokens per block, and the token
+    stride between (b, h) slices of the token tensors (0 = packed; the wrappers below fill
+    it in from the tensors they are given)."""
 
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
-                ("tokens_per_frame", ctypes.c_int32), ("block_size", ctypes.c_int32)]
+                ("tokens_per_frame", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("head_stride", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"Geom(B={self.B}, H={self.H}, d={self.d}, tpf={self.tokens_per_frame}, "
-                f"bs={self.block_size})")
+                f"bs={self.block_size}, head_stride={self.head_stride})")
+
+    def with_stride(self, head_stride: int) -> "Geom":
+        return Geom(self.B, self.H, self.d, self.tokens_per_frame, self.block_size, head_stride)
 
 
 def n_bpf(g: Geom) -> int:
@@ -101,6 +107,26 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _tokens(t: torch.Tensor, name: str, g: Geom, n_tokens: int) -> int:
+    """Checks a [B, H, n_tokens, d] token tensor whose (b, h) slices are contiguous and
+    evenly spaced (a packed tensor, or a token-range view of a bigger one); returns its
+    head stride in tokens."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if tuple(t.shape) != (g.B, g.H, n_tokens, g.d):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(g.B, g.H, n_tokens, g.d)}")
+    sb, sh, st, sc = t.stride()
+    if sc != 1 or st != g.d or sh % g.d != 0 or (g.B > 1 and sb != g.H * sh):
+        raise ValueError(f"{name}: each (b, h) slice must be contiguous and the slices evenly spaced")
+    return sh // g.d
+
+
+def _common_stride(g: Geom, strides: Sequence[int]) -> Geom:
+    if len(set(strides)) != 1:
+        raise ValueError(f"token tensors of one call must share their head stride, got {strides}")
+    return g.with_stride(strides[0])
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return LF_BF16
@@ -145,7 +171,8 @@ def lf_pool(x: torch.Tensor, g: Geom, n_frames: int, blk_out: Optional[torch.Ten
         blk_out = torch.empty((g.B, g.H, n_frames * nb, g.d), dtype=torch.float32, device=x.device)
     if frm_out is None and with_frames:
         frm_out = torch.empty((g.B, g.H, n_frames, g.d), dtype=torch.float32, device=x.device)
-    _check(lib.lf_pool(_dev(x, "x"), _dtype_code(x), g, n_frames, _dev(blk_out, "blk_out"),
+    gx = g.with_stride(_tokens(x, "x", g, n_frames * g.tokens_per_frame))
+    _check(lib.lf_pool(x.data_ptr(), _dtype_code(x), gx, n_frames, _dev(blk_out, "blk_out"),
                        None if frm_out is None else _dev(frm_out, "frm_out"), _stream(x)))
     return blk_out, frm_out
 
@@ -186,7 +213,10 @@ def lf_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geom, n
         out = torch.empty_like(q)
     if not (q.dtype == k.dtype == v.dtype == out.dtype):
         raise TypeError("q, k, v and out must share a dtype")
-    _check(lib.lf_sparse_attn(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                              _dtype_code(q), g, n_qframes, n_kframes, _dev(blocks, "blocks"),
+    lq, lk = n_qframes * g.tokens_per_frame, n_kframes * g.tokens_per_frame
+    strides = [_tokens(q, "q", g, lq), _tokens(k, "k", g, lk), _tokens(v, "v", g, lk), _tokens(out, "out", g, lq)]
+    ga = g.with_stride(0) if strides == [lq, lk, lk, lq] else _common_stride(g, strides)
+    _check(lib.lf_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              _dtype_code(q), ga, n_qframes, n_kframes, _dev(blocks, "blocks"),
                               blocks.shape[-1], float(scale), _stream(q)))
     return out

@@ -36,6 +36,7 @@ lf_status check_geom(const lf_geom& g, const char* fn) {
   if (g.block_size < 1 || g.block_size > g.tokens_per_frame)
     return fail(LF_ERR_INVALID_ARG, "%s: block_size must be in [1, tokens_per_frame]", fn);
   if (g.d < 1) return fail(LF_ERR_INVALID_ARG, "%s: d must be >= 1", fn);
+  if (g.head_stride < 0) return fail(LF_ERR_INVALID_ARG, "%s: head_stride must be >= 0", fn);
   if (g.d != 64 && g.d != 128) return fail(LF_ERR_UNSUPPORTED, "%s: d=%d unsupported (64 or 128)", fn, g.d);
   return LF_OK;
 }
@@ -125,11 +126,15 @@ lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float
     return fail(LF_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
   const int n_bpf = n_bpf_of(g);
   const long long BH = static_cast<long long>(g.B) * g.H;
-  if (!fits_int(BH * n_frames * n_bpf) || !fits_int(static_cast<long long>(n_frames) * g.tokens_per_frame))
+  const long long len = static_cast<long long>(n_frames) * g.tokens_per_frame;
+  if (!fits_int(BH * n_frames * n_bpf) || !fits_int(len))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  if (g.head_stride != 0 && g.head_stride < len)
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < n_frames*tpf = %lld", fn, g.head_stride, len);
+  const long long stride = g.head_stride ? g.head_stride : len;
   pending_error();
   return hip_status(lf::launch_pool(x, dt == LF_BF16, g.d, static_cast<int>(BH), n_frames,
-                                    g.tokens_per_frame, g.block_size, n_bpf, blk_out, frm_out,
+                                    g.tokens_per_frame, g.block_size, n_bpf, stride, blk_out, frm_out,
                                     static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -226,13 +231,19 @@ lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, l
   const long long n_kb = static_cast<long long>(n_kframes) * n_bpf;
   const long long lq = static_cast<long long>(n_qframes) * g.tokens_per_frame;
   const long long lk = static_cast<long long>(n_kframes) * g.tokens_per_frame;
-  if (!fits_int(BH * n_qb) || !fits_int(n_kb) || !fits_int(lq) || !fits_int(lk))
+  // the bf16 kernel addresses one (b, h) slice of K and V with 32-bit byte offsets
+  if (!fits_int(BH * n_qb) || !fits_int(n_kb) || !fits_int(lq) || !fits_int(lk * g.d * 4))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  if (g.head_stride != 0 && (g.head_stride < lq || g.head_stride < lk))
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d is below the query or key token count", fn,
+                g.head_stride);
   lf::AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.blocks = blocks;
   a.BH = static_cast<int>(BH); a.n_qb = static_cast<int>(n_qb); a.n_kb = static_cast<int>(n_kb);
   a.W_b = W_b; a.tpf = g.tokens_per_frame; a.bs = g.block_size; a.n_bpf = n_bpf;
   a.lq = static_cast<int>(lq); a.lk = static_cast<int>(lk);
+  a.q_stride = g.head_stride ? g.head_stride : lq;
+  a.kv_stride = g.head_stride ? g.head_stride : lk;
   a.scale_log2 = scale * 1.4426950408889634f;
   pending_error();
   const hipStream_t st = static_cast<hipStream_t>(stream);

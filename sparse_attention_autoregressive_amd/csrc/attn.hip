@@ -45,14 +45,14 @@ __global__ void __launch_bounds__(128) attn_f32_kernel(AttnArgs a) {
   const int t = threadIdx.x;
 
   const float* Q = static_cast<const float*>(a.q) +
-                   (static_cast<size_t>(bh) * a.lq + q_start + min(t, q_len - 1)) * D;
+                   (static_cast<size_t>(bh) * a.q_stride + q_start + min(t, q_len - 1)) * D;
   float q[D], o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) { q[c] = Q[c]; o[c] = 0.f; }
   float m = -1e30f, lsum = 0.f;
 
-  const float* K = static_cast<const float*>(a.k) + static_cast<size_t>(bh) * a.lk * D;
-  const float* V = static_cast<const float*>(a.v) + static_cast<size_t>(bh) * a.lk * D;
+  const float* K = static_cast<const float*>(a.k) + static_cast<size_t>(bh) * a.kv_stride * D;
+  const float* V = static_cast<const float*>(a.v) + static_cast<size_t>(bh) * a.kv_stride * D;
   const int* bl = a.blocks + static_cast<size_t>(row) * a.W_b;
 
   for (int n = 0; n < a.W_b; ++n) {
@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(128) attn_f32_kernel(AttnArgs a) {
   }
   if (t < q_len) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    float* O = static_cast<float*>(a.o) + (static_cast<size_t>(bh) * a.lq + q_start + t) * D;
+    float* O = static_cast<float*>(a.o) + (static_cast<size_t>(bh) * a.q_stride + q_start + t) * D;
 #pragma unroll
     for (int c = 0; c < D; c += 4)
       *reinterpret_cast<float4*>(O + c) = make_float4(o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv);
@@ -299,10 +299,10 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   const int q_start = geo.start(r), q_len = geo.len(r);
   const int nq = min(max(q_len - 32 * w, 0), 32);
 
-  const __bf16* Qg = static_cast<const __bf16*>(a.q) + static_cast<size_t>(bh) * a.lq * D;
+  const __bf16* Qg = static_cast<const __bf16*>(a.q) + static_cast<size_t>(bh) * a.q_stride * D;
   const uint32_t kv_bytes = static_cast<uint32_t>(a.lk) * ROWB;
-  const rsrc_t kr = make_rsrc(static_cast<const __bf16*>(a.k) + static_cast<size_t>(bh) * a.lk * D, kv_bytes);
-  const rsrc_t vr = make_rsrc(static_cast<const __bf16*>(a.v) + static_cast<size_t>(bh) * a.lk * D, kv_bytes);
+  const rsrc_t kr = make_rsrc(static_cast<const __bf16*>(a.k) + static_cast<size_t>(bh) * a.kv_stride * D, kv_bytes);
+  const rsrc_t vr = make_rsrc(static_cast<const __bf16*>(a.v) + static_cast<size_t>(bh) * a.kv_stride * D, kv_bytes);
 
   L s;
   {
@@ -407,7 +407,7 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   const float lt = s.lsum[0];                 // both key halves already summed
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (j < nq) {
-    __bf16* op = static_cast<__bf16*>(a.o) + (static_cast<size_t>(bh) * a.lq + q_start + 32 * w + j) * D;
+    __bf16* op = static_cast<__bf16*>(a.o) + (static_cast<size_t>(bh) * a.q_stride + q_start + 32 * w + j) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll

@@ -12,8 +12,9 @@ struct FrameSets {
   uint64_t forced[4];
 };
 
+// x_stride: tokens between consecutive (b, h) slices of x.
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
-                       int n_bpf, float* blk, float* frm, hipStream_t st);
+                       int n_bpf, long long x_stride, float* blk, float* frm, hipStream_t st);
 
 hipError_t launch_select_frames(const float* q_blk, const float* k_frm, int d, int BH, int n_qb,
                                 int n_kframes, const FrameSets& sets, int n_mem, int k_eff,
@@ -32,6 +33,8 @@ struct AttnArgs {
   int BH, n_qb, n_kb, W_b;
   int tpf, bs, n_bpf;
   int lq, lk;           // query / key tokens per (b, h)
+  long long q_stride;   // tokens between (b, h) slices of q and o
+  long long kv_stride;  // tokens between (b, h) slices of k and v
   float scale_log2;     // softmax scale * log2(e)
 };
 

@@ -38,7 +38,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256) pool_blocks_kernel(const T* __restrict__ x,
                                                           float* __restrict__ blk,
                                                           int n_frames, int tpf, int bs,
-                                                          int n_bpf) {
+                                                          int n_bpf, long long x_stride) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int C = D / E;           // chunks per token
   constexpr int P = 256 / C;         // tokens in flight per pass
@@ -49,7 +49,7 @@ __global__ void __launch_bounds__(256) pool_blocks_kernel(const T* __restrict__ 
   const int gb = blockIdx.x - bh * nb;
   const int f = gb / n_bpf, j = gb - f * n_bpf;
   const int len = min(bs, tpf - j * bs);
-  const T* base = x + (static_cast<size_t>(bh) * n_frames * tpf + f * tpf + j * bs) * D;
+  const T* base = x + (static_cast<size_t>(bh) * x_stride + f * tpf + j * bs) * D;
 
   const int c = threadIdx.x % C, s = threadIdx.x / C;
   float acc[E];
@@ -100,10 +100,10 @@ __global__ void __launch_bounds__(D) frame_means_kernel(const float* __restrict_
 
 template <typename T, int D>
 static hipError_t launch_pool_t(const void* x, int BH, int n_frames, int tpf, int bs, int n_bpf,
-                                float* blk, float* frm, hipStream_t st) {
+                                long long x_stride, float* blk, float* frm, hipStream_t st) {
   const unsigned nblk = static_cast<unsigned>(BH) * n_frames * n_bpf;
   hipLaunchKernelGGL((pool_blocks_kernel<T, D>), dim3(nblk), dim3(256), 0, st,
-                     static_cast<const T*>(x), blk, n_frames, tpf, bs, n_bpf);
+                     static_cast<const T*>(x), blk, n_frames, tpf, bs, n_bpf, x_stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || frm == nullptr) return e;
   hipLaunchKernelGGL((frame_means_kernel<D>), dim3(static_cast<unsigned>(BH) * n_frames), dim3(D),
@@ -112,13 +112,13 @@ static hipError_t launch_pool_t(const void* x, int BH, int n_frames, int tpf, in
 }
 
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
-                       int n_bpf, float* blk, float* frm, hipStream_t st) {
+                       int n_bpf, long long x_stride, float* blk, float* frm, hipStream_t st) {
   if (bf16) {
-    return d == 128 ? launch_pool_t<__bf16, 128>(x, BH, n_frames, tpf, bs, n_bpf, blk, frm, st)
-                    : launch_pool_t<__bf16, 64>(x, BH, n_frames, tpf, bs, n_bpf, blk, frm, st);
+    return d == 128 ? launch_pool_t<__bf16, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st)
+                    : launch_pool_t<__bf16, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st);
   }
-  return d == 128 ? launch_pool_t<float, 128>(x, BH, n_frames, tpf, bs, n_bpf, blk, frm, st)
-                  : launch_pool_t<float, 64>(x, BH, n_frames, tpf, bs, n_bpf, blk, frm, st);
+  return d == 128 ? launch_pool_t<float, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st)
+                  : launch_pool_t<float, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st);
 }
 
 }  // namespace lf

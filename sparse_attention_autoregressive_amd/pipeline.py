@@ -8,12 +8,13 @@ calls (timing loops, the per-layer sweep) allocate nothing.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
-from typing import Sequence
+from dataclasses import dataclass, field
+from typing import List, Sequence
 
 import torch
 
-from . import (Geom, lf_pool, lf_select_blocks, lf_select_frames, lf_sparse_attn, n_bpf)
+from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_select_blocks, lf_select_frames,
+               lf_sparse_attn, n_bpf)
 
 
 @dataclass
@@ -47,9 +48,10 @@ class ChunkPlan:
 
 
 class Workspace:
-    """Preallocated intermediates and output for one ChunkPlan."""
+    """Preallocated intermediates and output for one ChunkPlan (the output is left out
+    when the caller provides its own, as the sweep below does)."""
 
-    def __init__(self, plan: ChunkPlan, dtype: torch.dtype, device):
+    def __init__(self, plan: ChunkPlan, dtype: torch.dtype, device, with_output: bool = True):
         g = plan.geom
         f32, i32 = torch.float32, torch.int32
         self.plan = plan
@@ -58,7 +60,8 @@ class Workspace:
         self.k_frm = torch.empty((g.B, g.H, plan.n_kframes, g.d), dtype=f32, device=device)
         self.frames = torch.empty((g.B, g.H, plan.n_qb, plan.W_f), dtype=i32, device=device)
         self.blocks = torch.empty((g.B, g.H, plan.n_qb, plan.W_b), dtype=i32, device=device)
-        self.o = torch.empty((g.B, g.H, plan.n_qframes * g.tokens_per_frame, g.d), dtype=dtype, device=device)
+        self.o = (torch.empty((g.B, g.H, plan.n_qframes * g.tokens_per_frame, g.d), dtype=dtype, device=device)
+                  if with_output else None)
 
 
 def pool_q(ws: Workspace, q: torch.Tensor):
@@ -82,16 +85,110 @@ def select_blocks(ws: Workspace):
     lf_select_blocks(ws.q_blk, ws.k_blk, p.geom, p.n_qb, p.n_kframes, ws.frames, p.k_b, out=ws.blocks)
 
 
-def attend(ws: Workspace, q, k, v):
+def attend(ws: Workspace, q, k, v, out=None):
     p = ws.plan
-    lf_sparse_attn(q, k, v, p.geom, p.n_qframes, p.n_kframes, ws.blocks, p.scale, out=ws.o)
+    lf_sparse_attn(q, k, v, p.geom, p.n_qframes, p.n_kframes, ws.blocks, p.scale,
+                   out=ws.o if out is None else out)
 
 
-def hsa_chunk(ws: Workspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> torch.Tensor:
-    """Pool, select and attend for one chunk; returns ws.o (enqueued on the current stream)."""
+def hsa_chunk(ws: Workspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out=None) -> torch.Tensor:
+    """Pool, select and attend for one chunk; returns the output (enqueued on the current
+    stream). q, k, v and out may be token-range views of bigger per-head allocations."""
     pool_q(ws, q)
     pool_k(ws, k)
     select_frames(ws)
     select_blocks(ws)
-    attend(ws, q, k, v)
-    return ws.o
+    attend(ws, q, k, v, out)
+    return ws.o if out is None else out
+
+
+# ------------------------------------------------------------------ Chunk-Aware Growth sweep
+@dataclass
+class SweepPlan:
+    """The schedule of one clip under Chunk-Aware Growth (Light Forcing summary,
+    execution flow, stage 1; technical summary section 2.1): chunk i (1-based) queries
+    its frames_per_chunk frames against the key prefix of frames_per_chunk*i frames, with
+    sparsity s[i-1] from the CAG schedule and k_b from the block budget. A chunk with
+    s = 0 (the first) runs dense attention over the full block list."""
+
+    geom: Geom
+    frames_per_chunk: int
+    s: List[float]
+    beta: float
+    chunks: List[ChunkPlan] = field(default_factory=list)
+
+    @property
+    def n_chunks(self) -> int:
+        return len(self.chunks)
+
+    @property
+    def n_frames(self) -> int:
+        return self.frames_per_chunk * self.n_chunks
+
+    def dense(self, i: int) -> bool:
+        return self.s[i - 1] == 0.0
+
+
+def plan_sweep(g: Geom, n_chunks: int, frames_per_chunk: int, k_f: int, T: int, s_base: float,
+               s_target: float, scale: float, sink: Sequence[int] = (0,)) -> SweepPlan:
+    """CAG schedule (once per clip) and per-chunk plans. The FLOP weight of chunk i is its
+    dense attention work, query tokens times key tokens (proportional to i)."""
+    fpc, tpf, nb = frames_per_chunk, g.tokens_per_frame, n_bpf(g)
+    flops = [float(fpc * tpf * fpc * i * tpf) for i in range(1, n_chunks + 1)]
+    s, beta = lf_cag_schedule(n_chunks, T, s_base, s_target, flops)
+    sp = SweepPlan(g, fpc, s, beta)
+    for i in range(1, n_chunks + 1):
+        cur = list(range(fpc * (i - 1), fpc * i))
+        forced = sorted(set(sink) | set(cur))
+        mem = [f for f in range(fpc * (i - 1)) if f not in forced]
+        W_f = len(forced) + min(k_f, len(mem))
+        k_b = lf_block_budget(s[i - 1], fpc * i * nb, W_f, nb)
+        sp.chunks.append(ChunkPlan(g, fpc, fpc * i, mem, forced, k_f, k_b, scale))
+    return sp
+
+
+class SweepWorkspace:
+    """Per-chunk workspaces of a SweepPlan (reused by every layer), plus the full block
+    lists of the dense chunks."""
+
+    def __init__(self, sp: SweepPlan, dtype: torch.dtype, device):
+        g = sp.geom
+        self.plan = sp
+        self.chunks = [Workspace(p, dtype, device, with_output=False) for p in sp.chunks]
+        self.full = {}
+        for i, p in enumerate(sp.chunks, 1):
+            if sp.dense(i):
+                n_kb = p.n_kframes * p.n_bpf
+                ids = torch.arange(n_kb, dtype=torch.int32, device=device)
+                self.full[i] = ids.expand(g.B, g.H, p.n_qb, n_kb).contiguous()
+
+
+def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                o: torch.Tensor, mark=None) -> torch.Tensor:
+    """All chunks of one layer in order. q, k, v, o: [B, H, n_frames*tpf, d] holding the
+    whole clip; chunk i reads its query frames and the key prefix as views and writes its
+    frames of o. Enqueued on the current stream; returns o. `mark(i, stage)`, if given,
+    is called before each stage ("pool_q", "pool_k", "select_frames", "select_blocks",
+    "attn") and with stage "end" after chunk i (e.g. to record timing events)."""
+    sp = sw.plan
+    tpf = sp.geom.tokens_per_frame
+    tick = mark if mark is not None else (lambda i, stage: None)
+    for i, (p, ws) in enumerate(zip(sp.chunks, sw.chunks), 1):
+        a, b = (i - 1) * sp.frames_per_chunk * tpf, i * sp.frames_per_chunk * tpf
+        qv, ov, kv, vv = q[:, :, a:b], o[:, :, a:b], k[:, :, :b], v[:, :, :b]
+        if sp.dense(i):
+            tick(i, "attn")
+            lf_sparse_attn(qv, kv, vv, p.geom, p.n_qframes, p.n_kframes, sw.full[i], p.scale, out=ov)
+        else:
+            tick(i, "pool_q")
+            pool_q(ws, qv)
+            tick(i, "pool_k")
+            pool_k(ws, kv)
+            tick(i, "select_frames")
+            select_frames(ws)
+            tick(i, "select_blocks")
+            select_blocks(ws)
+            tick(i, "attn")
+            attend(ws, qv, kv, vv, ov)
+        tick(i, "end")
+    return o

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
             "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lf.lf_abi_version() == 1
+    assert lf.lf_abi_version() == 2
 
 
 @pytest.mark.parametrize("n,T,s_base,s_t", [(7, 4, 0.95, 0.8), (7, 4, 0.95, 0.85), (5, 2, 0.9, 0.6),
@@ -157,6 +157,19 @@ def test_sparse_attn_validation():
     _err(c.lf_sparse_attn(F, F, F, F, 3, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_UNSUPPORTED)
     _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 80, 1560, 64), 3, 21, F, 64, 0.1, None),
          lf.LF_ERR_UNSUPPORTED)
+
+
+def test_head_stride_validation():
+    c = _c()
+    F = FAKE
+    # pooling 3 frames of 1560 tokens needs a head stride of 0 or >= 4680
+    _err(c.lf_pool(F, 1, lf.Geom(1, 2, 128, 1560, 64, 4679), 3, F, None, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool(F, 1, lf.Geom(1, 2, 128, 1560, 64, -1), 3, F, None, None), lf.LF_ERR_INVALID_ARG)
+    # attention: the stride covers both the query (3 frames) and key (21 frames) ranges
+    _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 21 * 1560 - 1), 3, 21, F, 64, 0.1, None),
+         lf.LF_ERR_INVALID_ARG)
+    g = lf.Geom(1, 2, 128, 1560, 64)
+    assert g.head_stride == 0 and g.with_stride(7).head_stride == 7
 
 
 def test_error_message_is_per_thread():

@@ -1,0 +1,83 @@
+"""GPU parity of the Chunk-Aware Growth sweep (7 chunks of a 480p clip, one layer at a
+time), run as the sweep driver runs it: token-range views of per-layer Q/K/V/O tensors
+that hold the whole clip. On layers 0 and 29 every chunk's masks (every row) and
+outputs (sampled rows; the dense first chunk included) are compared with the oracle run
+on that chunk's slice of the layer."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import sparse_attention_autoregressive_amd as lf
+from sparse_attention_autoregressive_amd.pipeline import SweepWorkspace, plan_sweep, sweep_layer
+from support import compare_attention, compare_masks, log, oracle_k_b, run_oracle_masks, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("layer", [0, 29])
+def test_sweep_layer_parity(layer):
+    s = synth.SWEEP
+    g = lf.Geom(s.B, s.H, s.d, s.tpf, s.bs)
+    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5)
+    log(f"[sweep] layer {layer}: generating inputs")
+    x = synth.make_sweep_layer(s, layer)
+    dev = torch.device("cuda")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    o = torch.full_like(q, float("nan"))
+    sw = SweepWorkspace(sp, q.dtype, dev)
+    log(f"[sweep] layer {layer}: running 7 chunks on the GPU")
+    sweep_layer(sw, q, k, v, o)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any(), "some output token was not written"
+    q64, k64, v64 = x.np64()
+    o_np = o.float().cpu().numpy()
+    tpf, fpc = s.tpf, s.frames_per_chunk
+    for i, p in enumerate(sp.chunks, 1):
+        w = s.chunk(i, layer)
+        assert p.k_b == oracle_k_b(w)
+        a, b = (i - 1) * fpc * tpf, i * fpc * tpf
+        qi, ki, vi = q64[:, :, a:b], k64[:, :, :b], v64[:, :, :b]
+        ref = run_oracle_masks(w, qi, ki, p.k_b)
+        if sp.dense(i):
+            blocks = sw.full[i].cpu().numpy()
+            assert np.array_equal(ref["blocks"], blocks), "dense chunk: oracle lists are not the full lists"
+        else:
+            ws = sw.chunks[i - 1]
+            gpu = dict(frames=ws.frames.cpu().numpy(), blocks=ws.blocks.cpu().numpy())
+            stats = compare_masks(gpu, ref, min(p.k_b, p.n_bpf))
+            log(f"[sweep] layer {layer} chunk {i}: masks {stats}")
+            blocks = gpu["blocks"]
+        rows = sample_rows(w, p.n_qb, full=False)
+        st = compare_attention(w, dict(blocks=blocks, o=o_np[:, :, a:b]), qi, ki, vi, rows, "bf16")
+        log(f"[sweep] layer {layer} chunk {i} (k_b={p.k_b}, W_b={p.W_b}): attention {st}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_token_range_views_equal_packed(dtype):
+    """The whole path on token-range views of a larger allocation (head stride > token
+    count) gives bitwise the same pooled tensors, lists and outputs as on packed copies."""
+    from dataclasses import replace
+    from sparse_attention_autoregressive_amd.pipeline import Workspace, hsa_chunk
+    from support import plan_of, lib_k_b
+    w = replace(synth.TINY, dtype=dtype, name=f"tiny_views_{dtype}")
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    plan = plan_of(w, lib_k_b(w))
+    packed = Workspace(plan, q.dtype, dev)
+    hsa_chunk(packed, q, k, v)
+    cap = w.lk + 3 * w.tpf                                   # room for 3 more frames per head
+    big = {n: torch.full((w.B, w.H, cap, w.d), float("nan"), dtype=q.dtype, device=dev) for n in "qkvo"}
+    off = 2 * w.tpf                                          # queries start 2 frames in
+    big["q"][:, :, off:off + w.lq] = q
+    big["k"][:, :, :w.lk] = k
+    big["v"][:, :, :w.lk] = v
+    views = Workspace(plan, q.dtype, dev)
+    hsa_chunk(views, big["q"][:, :, off:off + w.lq], big["k"][:, :, :w.lk], big["v"][:, :, :w.lk],
+              out=big["o"][:, :, off:off + w.lq])
+    torch.cuda.synchronize()
+    for name in ("q_blk", "k_blk", "k_frm", "frames", "blocks"):
+        assert torch.equal(getattr(packed, name), getattr(views, name)), name
+    assert torch.equal(packed.o, big["o"][:, :, off:off + w.lq])
+    assert torch.isnan(big["o"][:, :, :off]).all() and torch.isnan(big["o"][:, :, off + w.lq:]).all()
