@@ -1,13 +1,16 @@
 """Benchmark of the HSA hot path on one MI355X.
 
 One step = one chunk of one layer through the whole path: the CAG schedule and block
-budget on the host, then pool Q, pool K (block + frame means), frame top-k, block top-k
-and block-sparse attention on the GPU, each a C-ABI call on torch's current stream.
-Default workload: the 480p layer at chunk 7 of 7 (12 heads x 128, 4680 query tokens
-against 21 frames = 32760 key tokens, 64-token blocks, 8 frames x 8 blocks per row).
+budget on the host, then pool Q, pool K (block + frame means), selection (frame top-k and
+block top-k in one launch) and block-sparse attention on the GPU, each a C-ABI call on
+torch's current stream.
+Default workload: the 480p layer at chunk 2 of 7 (12 heads x 128, 4680 query tokens
+against 6 frames = 9360 key tokens, 64-token blocks, CAG sparsity s_2 -> 6 frames x 6
+blocks per row); --workload selects the chunk-7 layer, the 69-frame long-memory layer,
+the tiny case or the full 30-layer x 7-chunk CAG sweep.
 
-Steps cycle over R independent layers' inputs (each ~230 MB of Q/K/V, R*230 MB well
-above the 256 MB Infinity Cache), so every step streams its K/V from HBM as in a real
+Steps cycle over R independent layers' inputs (R chosen so that together they exceed
+twice the 256 MB Infinity Cache), so every step streams its K/V from HBM as in a real
 layer-by-layer rollout. Inputs are resident in HBM before timing starts.
 
 Printed: one JSON line with the headline (dense-equivalent HSA TFLOP/s), per-kernel
@@ -33,13 +36,13 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 import sparse_attention_autoregressive_amd as lf  # noqa: E402
 from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, SweepWorkspace, Workspace,  # noqa: E402
-                                                          attend, plan_sweep, pool_k, pool_q, select_blocks,
-                                                          select_frames, sweep_layer)
+                                                          attend, plan_sweep, pool_k, pool_q, select,
+                                                          sweep_layer)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "HSA effective TFLOP/s (dense-equiv) + % MFMA peak + select overhead %, 480p"
-KERNELS = ["pool_q", "pool_k", "select_frames", "select_blocks", "attn"]
+KERNELS = ["pool_q", "pool_k", "select", "attn"]
 
 
 def chunk_flops(w):
@@ -94,6 +97,12 @@ def run_cpu_baseline(w, k_b: int, heads: int, min_s: float):
     return dense * reps / dt / 1e12, dt, reps, dense
 
 
+def hold_stream(ms: float = 50.0):
+    """Enqueues a spin kernel of about `ms` milliseconds on the current stream, so that the
+    host can queue the next calls before the GPU reaches them."""
+    torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -109,7 +118,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="480p_chunk2of7", choices=sorted(synth.WORKLOADS) + [synth.SWEEP.name])
-    ap.add_argument("--layers", type=int, default=4, help="independent input sets cycled per step")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="independent input sets cycled per step (0: enough to exceed 512 MB)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-min-s", type=float, default=10.0, help="repeat the CPU sample for at least this long")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -136,6 +146,10 @@ def main():
     plan = ChunkPlan(g, w.n_qframes, w.n_kframes, list(w.mem), list(w.forced), w.k_f, k_b, w.scale)
 
     # inputs: layer 0 from the seeded host generator, the others drawn on the device
+    esz = 2 if w.dtype == "bf16" else 4
+    set_bytes = w.B * w.H * (2 * w.lq + 2 * w.lk) * w.d * esz          # q, o, k, v
+    if args.layers <= 0:
+        args.layers = max(2, -(-(512 << 20) // set_bytes))
     print(f"[bench] generating {args.layers} input sets for {w.name}", file=sys.stderr, flush=True)
     x = synth.make(w)
     sets = [(x.q.to(dev), x.k.to(dev), x.v.to(dev))]
@@ -160,8 +174,8 @@ def main():
         lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
         ws = wss[i % len(sets)]
         q, k, v = sets[i % len(sets)]
-        calls = [lambda: pool_q(ws, q), lambda: pool_k(ws, k), lambda: select_frames(ws),
-                 lambda: select_blocks(ws), lambda: attend(ws, q, k, v)]
+        calls = [lambda: pool_q(ws, q), lambda: pool_k(ws, k), lambda: select(ws),
+                 lambda: attend(ws, q, k, v)]
         for j, c in enumerate(calls):
             if ev is not None:
                 ev[j].record(stream)
@@ -174,14 +188,20 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # per-call times: the same steps again with events between calls, all enqueued while
+    # a spin kernel holds the stream, so host launch gaps do not show up as kernel time
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    hold_stream()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(KERNELS))]
                     for i in range(args.steps)]) * 1e3                      # us
     mean_us = per.mean(axis=0)
@@ -190,24 +210,21 @@ def main():
 
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
-    t_attn = mean_us[4] * 1e-6
+    t_attn = mean_us[3] * 1e-6
     t_path = mean_us.sum() * 1e-6
     attn_tflops = f_active / t_attn / 1e12
     value = f_dense / (ms_per_step * 1e-3) / 1e12
-    sel_pct = 100.0 * (mean_us[2] + mean_us[3]) / mean_us[4]
+    sel_pct = 100.0 * mean_us[2] / mean_us[3]
     pool_gbs = {
         "pool_q": pool_bytes(w, w.n_qframes, False) / (mean_us[0] * 1e-6) / 1e9,
         "pool_k": pool_bytes(w, w.n_kframes, True) / (mean_us[1] * 1e-6) / 1e9,
     }
     n_rows = w.B * w.H * plan.n_qb
-    sel_bytes = {
-        # q~ rows + the memory set's frame means per row + list writes
-        "select_frames": n_rows * (w.d * 4 + len(w.mem) * w.d * 4 + plan.W_f * 4),
-        # frames lists read, q~ per listed frame, each head's k~ once, list writes
-        "select_blocks": n_rows * (plan.W_f * 4 + plan.W_f * w.d * 4 + plan.W_b * 4)
-        + w.B * w.H * w.n_kframes * nb * w.d * 4,
-    }
-    sel_gbs = {k: sel_bytes[k] / (mean_us[2 + i] * 1e-6) / 1e9 for i, k in enumerate(sel_bytes)}
+    # algorithmic HBM bytes of the selection launch: q~ rows, each head's frame means and
+    # block means once (they stay in L2 across the head's rows), T_r and list writes
+    sel_bytes = (n_rows * (w.d * 4 + plan.W_f * 4 + plan.W_b * 4)
+                 + w.B * w.H * w.n_kframes * (nb + 1) * w.d * 4)
+    sel_gbs = {"select": sel_bytes / (mean_us[2] * 1e-6) / 1e9}
 
     cpu = None
     if args.cpu_heads > 0:
@@ -238,7 +255,7 @@ def main():
                    "cag_beta": beta, "input_sets": len(sets)},
         "mfma_pct_peak_active": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
         "select_overhead_pct": sel_pct,
-        "pool_select_pct_of_attn": 100.0 * (mean_us[:4].sum()) / mean_us[4],
+        "pool_select_pct_of_attn": 100.0 * (mean_us[:3].sum()) / mean_us[3],
         "dense_equiv_tflops_attn_only": f_dense / t_attn / 1e12,
         "dense_equiv_tflops_kernel_sum": f_dense / t_path / 1e12,
         "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
@@ -253,7 +270,7 @@ def main():
     print(json.dumps(line))
 
 
-STAGES = ["pool_q", "pool_k", "select_frames", "select_blocks", "attn"]
+STAGES = ["pool_q", "pool_k", "select", "attn"]
 
 
 def bench_sweep(args):
@@ -307,8 +324,10 @@ def bench_sweep(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    # per-stage breakdown from one extra evented sweep (events add host overhead)
+    # per-stage breakdown from one extra evented sweep, enqueued behind a spin kernel so
+    # that host launch gaps do not count as stage time
     events = []
+    hold_stream(400.0)
     run(events)
     torch.cuda.synchronize()
     stage_us = {st: 0.0 for st in STAGES}
@@ -350,7 +369,7 @@ def bench_sweep(args):
                    "cag_s": [round(x, 6) for x in sp.s], "cag_beta": sp.beta,
                    "k_b": [c.k_b for c in sp.chunks], "W_b": [c.W_b for c in sp.chunks]},
         "mfma_pct_peak_active": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
-        "select_overhead_pct": 100.0 * (stage_us["select_frames"] + stage_us["select_blocks"]) / stage_us["attn"],
+        "select_overhead_pct": 100.0 * stage_us["select"] / stage_us["attn"],
         "pool_select_pct_of_attn": 100.0 * (sum(stage_us.values()) - stage_us["attn"]) / stage_us["attn"],
         "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
         "stage_us_per_sweep": {k: round(v, 1) for k, v in stage_us.items()},

@@ -156,6 +156,22 @@ lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, in
                            int32_t* blocks_out, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * lf_select -- [S3] both selection stages in one launch: lf_select_frames followed by
+ * lf_select_blocks, with the same arguments, validation and results (bitwise), without
+ * the round trip of T_r through memory between two launches.
+ * q_blk, k_frm, k_blk: as above. mem, forced, k_f: as for lf_select_frames; W_f =
+ *   n_forced + min(k_f, n_mem). k_b: as for lf_select_blocks.
+ * frames_out: [B, H, n_qb, W_f] int32, or NULL to skip writing T_r.
+ * blocks_out: [B, H, n_qb, W_f*min(k_b, n_bpf)] int32.
+ * Limits: those of both calls (n_kframes <= 256, n_bpf <= 64).
+ * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_select(const float* q_blk, const float* k_frm, const float* k_blk, lf_geom g,
+                    int32_t n_qb, int32_t n_kframes, const int32_t* mem, int32_t n_mem,
+                    const int32_t* forced, int32_t n_forced, int32_t k_f, int32_t k_b,
+                    int32_t* frames_out, int32_t* blocks_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * lf_sparse_attn -- [S3], [G2.2] block-sparse attention: each query token t of query
  * block r attends only to the tokens of the blocks listed for r,
  *   o_t = sum_u softmax_u(scale * <q_t, k_u>) v_u   (softmax over the listed tokens).

@@ -80,6 +80,7 @@ def _load():
         "lf_pool": [vp, i32, Geom, i32, vp, vp, vp],
         "lf_select_frames": [vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, vp, vp],
         "lf_select_blocks": [vp, vp, Geom, i32, i32, vp, i32, i32, vp, vp],
+        "lf_select": [vp, vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, i32, vp, vp, vp],
         "lf_sparse_attn": [vp, vp, vp, vp, i32, Geom, i32, i32, vp, i32, f32, vp],
     }
     for name, args in sig.items():
@@ -202,6 +203,26 @@ def lf_select_blocks(q_blk: torch.Tensor, k_blk: torch.Tensor, g: Geom, n_qb: in
     _check(lib.lf_select_blocks(_dev(q_blk, "q_blk"), _dev(k_blk, "k_blk"), g, n_qb, n_kframes,
                                 _dev(frames, "frames"), W_f, k_b, _dev(out, "out"), _stream(q_blk)))
     return out
+
+
+def lf_select(q_blk: torch.Tensor, k_frm: torch.Tensor, k_blk: torch.Tensor, g: Geom, n_qb: int,
+              n_kframes: int, mem: Sequence[int], forced: Sequence[int], k_f: int, k_b: int,
+              frames_out: Optional[torch.Tensor] = None, blocks_out: Optional[torch.Tensor] = None,
+              with_frames: bool = True):
+    """Both selection stages in one launch: (T_r [B,H,n_qb,W_f] or None, lists [B,H,n_qb,W_b])."""
+    lib = _load()
+    W_f = len(forced) + min(k_f, len(mem))
+    W_b = max(W_f, 1) * min(k_b, n_bpf(g))
+    dev = q_blk.device
+    if frames_out is None and with_frames:
+        frames_out = torch.empty((g.B, g.H, n_qb, max(W_f, 1)), dtype=torch.int32, device=dev)
+    if blocks_out is None:
+        blocks_out = torch.empty((g.B, g.H, n_qb, W_b), dtype=torch.int32, device=dev)
+    _check(lib.lf_select(_dev(q_blk, "q_blk"), _dev(k_frm, "k_frm"), _dev(k_blk, "k_blk"), g, n_qb, n_kframes,
+                         _i32_array(mem), len(mem), _i32_array(forced), len(forced), k_f, k_b,
+                         None if frames_out is None else _dev(frames_out, "frames_out"),
+                         _dev(blocks_out, "blocks_out"), _stream(q_blk)))
+    return frames_out, blocks_out
 
 
 def lf_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geom, n_qframes: int,

@@ -51,6 +51,74 @@ lf_status hip_status(hipError_t e, const char* fn) {
   return fail(LF_ERR_HIP, "%s: HIP error %d (%s)", fn, static_cast<int>(e), hipGetErrorString(e));
 }
 
+// Checks of the frame stage shared by lf_select_frames and lf_select; fills the id lists.
+lf_status check_frame_stage(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
+                            int32_t n_kframes, const int32_t* mem, int32_t n_mem,
+                            const int32_t* forced, int32_t n_forced, int32_t k_f,
+                            lf::SelectArgs& a, const char* fn) {
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (n_qb < 1 || n_kframes < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_qb and n_kframes must be >= 1", fn);
+  if (n_kframes > lf::kMaxFrames)
+    return fail(LF_ERR_UNSUPPORTED, "%s: n_kframes=%d > %d", fn, n_kframes, lf::kMaxFrames);
+  if (n_mem < 0 || n_forced < 0 || k_f < 0) return fail(LF_ERR_INVALID_ARG, "%s: negative count", fn);
+  if ((n_mem > 0 && !mem) || (n_forced > 0 && !forced))
+    return fail(LF_ERR_INVALID_ARG, "%s: NULL frame-id array", fn);
+  if (!q_blk || !k_frm) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q_blk) || !aligned16(k_frm)) return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  bool seen[lf::kMaxFrames] = {};
+  bool in_mem[lf::kMaxFrames] = {};
+  for (int i = 0; i < n_mem; ++i) {
+    const int f = mem[i];
+    if (f < 0 || f >= n_kframes) return fail(LF_ERR_INVALID_ARG, "%s: mem[%d]=%d out of range", fn, i, f);
+    if (seen[f]) return fail(LF_ERR_INVALID_ARG, "%s: duplicate memory frame %d", fn, f);
+    seen[f] = in_mem[f] = true;
+    a.lists.mem[i] = static_cast<int16_t>(f);
+  }
+  for (int i = 0; i < n_forced; ++i) {
+    const int f = forced[i];
+    if (f < 0 || f >= n_kframes) return fail(LF_ERR_INVALID_ARG, "%s: forced[%d]=%d out of range", fn, i, f);
+    if (in_mem[f]) return fail(LF_ERR_INVALID_ARG, "%s: frame %d is both forced and in the memory set", fn, f);
+    if (seen[f]) return fail(LF_ERR_INVALID_ARG, "%s: duplicate forced frame %d", fn, f);
+    seen[f] = true;
+    a.lists.forced[i] = static_cast<int16_t>(f);
+  }
+  a.k_eff = k_f < n_mem ? k_f : n_mem;
+  a.W_f = n_forced + a.k_eff;
+  if (a.W_f < 1) return fail(LF_ERR_INVALID_ARG, "%s: empty frame set (W_f = 0)", fn);
+  if (!fits_int(static_cast<long long>(g.B) * g.H * n_qb))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  a.q_blk = q_blk;
+  a.k_frm = k_frm;
+  a.n_qb = n_qb;
+  a.n_kframes = n_kframes;
+  a.n_mem = n_mem;
+  a.n_forced = n_forced;
+  return LF_OK;
+}
+
+// Checks of the block stage shared by lf_select_blocks and lf_select.
+lf_status check_block_stage(const float* k_blk, lf_geom g, int32_t n_qb, int32_t n_kframes, int32_t W_f,
+                            int32_t k_b, int32_t* blocks_out, lf::SelectArgs& a, const char* fn) {
+  if (n_qb < 1 || n_kframes < 1 || W_f < 1 || k_b < 1)
+    return fail(LF_ERR_INVALID_ARG, "%s: n_qb, n_kframes, W_f and k_b must be >= 1", fn);
+  if (n_kframes > 65535) return fail(LF_ERR_UNSUPPORTED, "%s: n_kframes=%d > 65535", fn, n_kframes);
+  const int n_bpf = n_bpf_of(g);
+  if (n_bpf > 64) return fail(LF_ERR_UNSUPPORTED, "%s: %d blocks per frame > 64", fn, n_bpf);
+  if (!k_blk || !blocks_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(k_blk) || (reinterpret_cast<uintptr_t>(blocks_out) & 3u))
+    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  a.kb_eff = k_b < n_bpf ? k_b : n_bpf;
+  if (!fits_int(static_cast<long long>(g.B) * g.H * n_qb) || !fits_int(static_cast<long long>(W_f) * a.kb_eff))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  a.k_blk = k_blk;
+  a.blocks_out = blocks_out;
+  a.n_bpf = n_bpf;
+  a.n_qb = n_qb;
+  a.n_kframes = n_kframes;
+  a.W_f = W_f;
+  return LF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,41 +212,14 @@ lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, in
                            const int32_t* forced, int32_t n_forced, int32_t k_f,
                            int32_t* frames_out, void* stream) {
   const char* fn = "lf_select_frames";
-  if (lf_status st = check_geom(g, fn)) return st;
-  if (n_qb < 1 || n_kframes < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_qb and n_kframes must be >= 1", fn);
-  if (n_kframes > 256) return fail(LF_ERR_UNSUPPORTED, "%s: n_kframes=%d > 256", fn, n_kframes);
-  if (n_mem < 0 || n_forced < 0 || k_f < 0) return fail(LF_ERR_INVALID_ARG, "%s: negative count", fn);
-  if ((n_mem > 0 && !mem) || (n_forced > 0 && !forced))
-    return fail(LF_ERR_INVALID_ARG, "%s: NULL frame-id array", fn);
-  if (!q_blk || !k_frm || !frames_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-  if (!aligned16(q_blk) || !aligned16(k_frm) || (reinterpret_cast<uintptr_t>(frames_out) & 3u))
-    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
-  lf::FrameSets sets = {};
-  for (int i = 0; i < n_mem; ++i) {
-    const int f = mem[i];
-    if (f < 0 || f >= n_kframes) return fail(LF_ERR_INVALID_ARG, "%s: mem[%d]=%d out of range", fn, i, f);
-    if ((sets.mem[f >> 6] >> (f & 63)) & 1ull) return fail(LF_ERR_INVALID_ARG, "%s: duplicate memory frame %d", fn, f);
-    sets.mem[f >> 6] |= 1ull << (f & 63);
-  }
-  for (int i = 0; i < n_forced; ++i) {
-    const int f = forced[i];
-    if (f < 0 || f >= n_kframes) return fail(LF_ERR_INVALID_ARG, "%s: forced[%d]=%d out of range", fn, i, f);
-    if ((sets.forced[f >> 6] >> (f & 63)) & 1ull) return fail(LF_ERR_INVALID_ARG, "%s: duplicate forced frame %d", fn, f);
-    if ((sets.mem[f >> 6] >> (f & 63)) & 1ull)
-      return fail(LF_ERR_INVALID_ARG, "%s: frame %d is both forced and in the memory set", fn, f);
-    sets.forced[f >> 6] |= 1ull << (f & 63);
-  }
-  const int k_eff = k_f < n_mem ? k_f : n_mem;
-  const int W_f = n_forced + k_eff;
-  if (W_f < 1) return fail(LF_ERR_INVALID_ARG, "%s: empty frame set (W_f = 0)", fn);
-  const long long BH = static_cast<long long>(g.B) * g.H;
-  if (!fits_int(BH * ((n_qb + 15) / 16)) || !fits_int(BH * n_qb))
-    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  lf::SelectArgs a = {};
+  if (lf_status st = check_frame_stage(q_blk, k_frm, g, n_qb, n_kframes, mem, n_mem, forced, n_forced, k_f, a, fn))
+    return st;
+  if (!frames_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (reinterpret_cast<uintptr_t>(frames_out) & 3u) return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  a.frames_out = frames_out;
   pending_error();
-  return hip_status(lf::launch_select_frames(q_blk, k_frm, g.d, static_cast<int>(BH), n_qb, n_kframes,
-                                             sets, n_mem, k_eff, W_f, frames_out,
-                                             static_cast<hipStream_t>(stream)),
-                    fn);
+  return hip_status(lf::launch_select(a, g.d, g.B * g.H * n_qb, true, false, static_cast<hipStream_t>(stream)), fn);
 }
 
 lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, int32_t n_qb,
@@ -186,25 +227,31 @@ lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, in
                            int32_t* blocks_out, void* stream) {
   const char* fn = "lf_select_blocks";
   if (lf_status st = check_geom(g, fn)) return st;
-  if (n_qb < 1 || n_kframes < 1 || W_f < 1 || k_b < 1)
-    return fail(LF_ERR_INVALID_ARG, "%s: n_qb, n_kframes, W_f and k_b must be >= 1", fn);
-  if (n_kframes > 65535) return fail(LF_ERR_UNSUPPORTED, "%s: n_kframes=%d > 65535", fn, n_kframes);
-  const int n_bpf = n_bpf_of(g);
-  if (n_bpf > 64) return fail(LF_ERR_UNSUPPORTED, "%s: %d blocks per frame > 64", fn, n_bpf);
-  if (!q_blk || !k_blk || !frames || !blocks_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-  if (!aligned16(q_blk) || !aligned16(k_blk) || (reinterpret_cast<uintptr_t>(frames) & 3u) ||
-      (reinterpret_cast<uintptr_t>(blocks_out) & 3u))
+  lf::SelectArgs a = {};
+  if (lf_status st = check_block_stage(k_blk, g, n_qb, n_kframes, W_f, k_b, blocks_out, a, fn)) return st;
+  if (!q_blk || !frames) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q_blk) || (reinterpret_cast<uintptr_t>(frames) & 3u))
     return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
-  const int kb_eff = k_b < n_bpf ? k_b : n_bpf;
-  const long long BH = static_cast<long long>(g.B) * g.H;
-  const long long tiles = (n_qb + 15) / 16;
-  if (!fits_int(BH * n_kframes * tiles) || !fits_int(static_cast<long long>(W_f) * kb_eff))
-    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  a.q_blk = q_blk;
+  a.frames_in = frames;
   pending_error();
-  return hip_status(lf::launch_select_blocks(q_blk, k_blk, frames, g.d, static_cast<int>(BH), n_qb,
-                                             n_kframes, n_bpf, W_f, kb_eff, blocks_out,
-                                             static_cast<hipStream_t>(stream)),
-                    fn);
+  return hip_status(lf::launch_select(a, g.d, g.B * g.H * n_qb, false, true, static_cast<hipStream_t>(stream)), fn);
+}
+
+lf_status lf_select(const float* q_blk, const float* k_frm, const float* k_blk, lf_geom g, int32_t n_qb,
+                    int32_t n_kframes, const int32_t* mem, int32_t n_mem, const int32_t* forced,
+                    int32_t n_forced, int32_t k_f, int32_t k_b, int32_t* frames_out, int32_t* blocks_out,
+                    void* stream) {
+  const char* fn = "lf_select";
+  lf::SelectArgs a = {};
+  if (lf_status st = check_frame_stage(q_blk, k_frm, g, n_qb, n_kframes, mem, n_mem, forced, n_forced, k_f, a, fn))
+    return st;
+  if (lf_status st = check_block_stage(k_blk, g, n_qb, n_kframes, a.W_f, k_b, blocks_out, a, fn)) return st;
+  if (frames_out && (reinterpret_cast<uintptr_t>(frames_out) & 3u))
+    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  a.frames_out = frames_out;
+  pending_error();
+  return hip_status(lf::launch_select(a, g.d, g.B * g.H * n_qb, true, true, static_cast<hipStream_t>(stream)), fn);
 }
 
 lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, lf_dtype dt,

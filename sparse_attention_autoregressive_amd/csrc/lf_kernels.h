@@ -6,23 +6,35 @@
 
 namespace lf {
 
-// Memory set and always-kept frames as bit masks over frame ids < 256.
-struct FrameSets {
-  uint64_t mem[4];
-  uint64_t forced[4];
+constexpr int kMaxFrames = 256;   // key frames a frame-selecting call may address
+
+// Frame ids of the memory set M and of the always-kept frames, passed by value.
+struct FrameLists {
+  int16_t mem[kMaxFrames];
+  int16_t forced[kMaxFrames];
 };
 
 // x_stride: tokens between consecutive (b, h) slices of x.
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
                        int n_bpf, long long x_stride, float* blk, float* frm, hipStream_t st);
 
-hipError_t launch_select_frames(const float* q_blk, const float* k_frm, int d, int BH, int n_qb,
-                                int n_kframes, const FrameSets& sets, int n_mem, int k_eff,
-                                int W_f, int* out, hipStream_t st);
+// One launch of the selection kernel over n_rows = B*H*n_qb rows. Frame stage: reads
+// q_blk, k_frm, lists, n_mem, n_forced, k_eff and writes frames_out (if set). Block
+// stage: reads q_blk, k_blk and the frame lists (from the frame stage, else frames_in)
+// and writes blocks_out.
+struct SelectArgs {
+  const float* q_blk;
+  const float* k_frm;
+  const float* k_blk;
+  const int* frames_in;
+  int* frames_out;
+  int* blocks_out;
+  int n_qb, n_kframes, n_bpf;
+  int n_mem, n_forced, k_eff, W_f, kb_eff;
+  FrameLists lists;
+};
 
-hipError_t launch_select_blocks(const float* q_blk, const float* k_blk, const int* frames, int d,
-                                int BH, int n_qb, int n_kframes, int n_bpf, int W_f, int kb_eff,
-                                int* out, hipStream_t st);
+hipError_t launch_select(const SelectArgs& a, int d, int n_rows, bool frames, bool blocks, hipStream_t st);
 
 struct AttnArgs {
   const void* q;

@@ -2,8 +2,8 @@
 
 Order (Light Forcing summary, execution flow, stages 2-3): pool the chunk's queries
 (block means q~), pool all keys (block means k~ and frame means k^), frame top-k per
-query block (T_r), block top-k inside the chosen frames (the mask B_r as id lists),
-block-sparse attention. All outputs are allocated once in a `Workspace`, so repeated
+query block (T_r) and block top-k inside the chosen frames (the mask B_r as id lists)
+in one selection launch, block-sparse attention. All outputs are allocated once in a `Workspace`, so repeated
 calls (timing loops, the per-layer sweep) allocate nothing.
 """
 from __future__ import annotations
@@ -13,8 +13,8 @@ from typing import List, Sequence
 
 import torch
 
-from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_select_blocks, lf_select_frames,
-               lf_sparse_attn, n_bpf)
+from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_select, lf_select_blocks,
+               lf_select_frames, lf_sparse_attn, n_bpf)
 
 
 @dataclass
@@ -85,6 +85,13 @@ def select_blocks(ws: Workspace):
     lf_select_blocks(ws.q_blk, ws.k_blk, p.geom, p.n_qb, p.n_kframes, ws.frames, p.k_b, out=ws.blocks)
 
 
+def select(ws: Workspace):
+    """Both selection stages in one launch (same results as select_frames + select_blocks)."""
+    p = ws.plan
+    lf_select(ws.q_blk, ws.k_frm, ws.k_blk, p.geom, p.n_qb, p.n_kframes, p.mem, p.forced, p.k_f, p.k_b,
+              frames_out=ws.frames, blocks_out=ws.blocks)
+
+
 def attend(ws: Workspace, q, k, v, out=None):
     p = ws.plan
     lf_sparse_attn(q, k, v, p.geom, p.n_qframes, p.n_kframes, ws.blocks, p.scale,
@@ -96,8 +103,7 @@ def hsa_chunk(ws: Workspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     stream). q, k, v and out may be token-range views of bigger per-head allocations."""
     pool_q(ws, q)
     pool_k(ws, k)
-    select_frames(ws)
-    select_blocks(ws)
+    select(ws)
     attend(ws, q, k, v, out)
     return ws.o if out is None else out
 
@@ -168,8 +174,8 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
     """All chunks of one layer in order. q, k, v, o: [B, H, n_frames*tpf, d] holding the
     whole clip; chunk i reads its query frames and the key prefix as views and writes its
     frames of o. Enqueued on the current stream; returns o. `mark(i, stage)`, if given,
-    is called before each stage ("pool_q", "pool_k", "select_frames", "select_blocks",
-    "attn") and with stage "end" after chunk i (e.g. to record timing events)."""
+    is called before each stage ("pool_q", "pool_k", "select", "attn") and with stage
+    "end" after chunk i (e.g. to record timing events)."""
     sp = sw.plan
     tpf = sp.geom.tokens_per_frame
     tick = mark if mark is not None else (lambda i, stage: None)
@@ -184,10 +190,8 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
             pool_q(ws, qv)
             tick(i, "pool_k")
             pool_k(ws, kv)
-            tick(i, "select_frames")
-            select_frames(ws)
-            tick(i, "select_blocks")
-            select_blocks(ws)
+            tick(i, "select")
+            select(ws)
             tick(i, "attn")
             attend(ws, qv, kv, vv, ov)
         tick(i, "end")

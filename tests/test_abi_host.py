@@ -25,7 +25,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(lf.library_path())
     names = _declared()
-    assert {"lf_pool", "lf_select_frames", "lf_select_blocks", "lf_sparse_attn",
+    assert {"lf_pool", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
             "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -141,6 +141,23 @@ def test_select_blocks_validation():
     _err(c.lf_select_blocks(FAKE, FAKE, lf.Geom(1, 2, 128, 1560, 16), 75, 21, FAKE, 8, 8, FAKE, None),
          lf.LF_ERR_UNSUPPORTED)                                 # 98 blocks per frame
     _err(c.lf_select_blocks(None, FAKE, g, 75, 21, FAKE, 8, 8, FAKE, None), lf.LF_ERR_INVALID_ARG)
+
+
+def test_select_fused_validation():
+    c = _c()
+    g = lf.Geom(1, 2, 128, 1560, 64)
+    arr = lf._i32_array
+
+    def call(mem, forced, k_f=2, k_b=8, n_kf=10, frames=FAKE, blocks=FAKE, gg=g):
+        return c.lf_select(FAKE, FAKE, FAKE, gg, 75, n_kf, arr(mem), len(mem), arr(forced), len(forced),
+                           k_f, k_b, frames, blocks, None)
+
+    _err(call([1, 2], [2, 9]), lf.LF_ERR_INVALID_ARG)          # overlap
+    _err(call([1], [0], k_b=0), lf.LF_ERR_INVALID_ARG)
+    _err(call([1], [0], blocks=None), lf.LF_ERR_INVALID_ARG)
+    _err(call([1], [0], frames=FAKE + 2), lf.LF_ERR_INVALID_ARG)
+    _err(call([1], [0], n_kf=300), lf.LF_ERR_UNSUPPORTED)
+    _err(call([1], [0], gg=lf.Geom(1, 2, 128, 1560, 16)), lf.LF_ERR_UNSUPPORTED)   # 98 blocks per frame
 
 
 def test_sparse_attn_validation():

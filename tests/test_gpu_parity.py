@@ -185,3 +185,42 @@ def test_edge_constant_values():
     v = torch.full_like(x.v, 0.8125).to(dev)           # exactly representable in bf16
     gpu = run_gpu(w, x, w.k_b, v=v)
     assert np.abs(gpu["o"] - 0.8125).max() <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "480p_chunk7of7", "longlive_69f"])
+def test_separate_select_calls_equal_fused(name):
+    """lf_select_frames then lf_select_blocks give bitwise the lists of the fused lf_select
+    (which the pipeline runs), with and without writing T_r."""
+    w, x, _, gpu, _, k_b = _case(name)
+    dev = torch.device("cuda")
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    nb = lf.n_bpf(g)
+    n_qb = w.n_qframes * nb
+    q_blk, k_frm = (torch.from_numpy(gpu[k]).to(dev) for k in ("q_blk", "k_frm"))
+    k_blk = torch.from_numpy(gpu["k_blk"]).to(dev)
+    frames = lf.lf_select_frames(q_blk, k_frm, g, n_qb, w.n_kframes, w.mem, w.forced, w.k_f)
+    blocks = lf.lf_select_blocks(q_blk, k_blk, g, n_qb, w.n_kframes, frames, k_b)
+    _, blocks2 = lf.lf_select(q_blk, k_frm, k_blk, g, n_qb, w.n_kframes, w.mem, w.forced, w.k_f, k_b,
+                              with_frames=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(frames.cpu().numpy(), gpu["frames"])
+    assert np.array_equal(blocks.cpu().numpy(), gpu["blocks"])
+    assert np.array_equal(blocks2.cpu().numpy(), gpu["blocks"])
+
+
+def test_select_blocks_malformed_frames_stay_in_bounds():
+    """Frame ids outside [0, n_kframes) in the input of lf_select_blocks are clamped by the
+    kernel: the call completes and every listed id is a valid block id (the contract only
+    promises in-bounds behaviour for such rows)."""
+    w, x, _, gpu, _, k_b = _case("480p_chunk7of7")
+    dev = torch.device("cuda")
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    nb = lf.n_bpf(g)
+    frames = torch.from_numpy(gpu["frames"]).to(dev)
+    frames[..., 0] = -5
+    frames[..., -1] = 10 ** 6
+    q_blk, k_blk = (torch.from_numpy(gpu[k]).to(dev) for k in ("q_blk", "k_blk"))
+    blocks = lf.lf_select_blocks(q_blk, k_blk, g, w.n_qframes * nb, w.n_kframes, frames.contiguous(), k_b)
+    torch.cuda.synchronize()
+    b = blocks.cpu().numpy()
+    assert b.min() >= 0 and b.max() < w.n_kframes * nb
