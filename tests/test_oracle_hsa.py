@@ -22,33 +22,38 @@ import synth
 
 
 # ----------------------------------------------------------------------------- hand example
-def test_hand_worked_example():
-    """d=2, 2 tokens per frame, 1 token per block, key frames 0..3, the current chunk is
-    frame 3 (two 1-token query blocks), sink frame 0, M = {1, 2}, k_f = k_b = 1.
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
 
-    Keys per frame: f0 [1,0],[0,1]; f1 [2,0],[0,0]; f2 [0,2],[0,2]; f3 [1,1],[-1,1].
-    Frame means: f0 [.5,.5], f1 [1,0], f2 [0,2], f3 [0,1].
-    r0: q~ = [1,0]: p(1)=1 > p(2)=0 -> T_0 = {0,1,3}. Block scores: f0 (1,0) -> j0;
-        f1 (2,0) -> j0; f3 (1,-1) -> j0. List [0, 2, 6].
-    r1: q~ = [0,1]: p(1)=0 < p(2)=2 -> T_1 = {0,2,3}. f0 (0,1) -> j1; f2 (2,2) tie ->
-        lower index j0; f3 (1,1) tie -> j0. List [1, 4, 6].
-    V_t = [t, 1]. Attention, scale c = 1/sqrt(2):
-        r0 logits c*(1, 2, 1) over tokens (0, 2, 6): o = (2 e^{2c} + 6 e^{c}) / (2 e^{c} + e^{2c})
-        r1 logits c*(1, 2, 1) over tokens (1, 4, 6): o = (1 e^{c} + 4 e^{2c} + 6 e^{c}) / (2 e^{c} + e^{2c})
-    """
-    K = np.array([[1, 0], [0, 1], [2, 0], [0, 0], [0, 2], [0, 2], [1, 1], [-1, 1]], float)[None, None]
-    V = np.stack([np.arange(8.0), np.ones(8)], axis=1)[None, None]
-    Q = np.array([[1, 0], [0, 1]], float)[None, None]
+
+def _golden(name):
+    vals = {}
+    for line in open(__import__("os").path.join(GOLDEN, name)):
+        line = line.split("#", 1)[0].split()
+        if line:
+            vals[line[0]] = [float(x) for x in line[1:]]
+    return vals
+
+
+def test_hand_worked_example():
+    """The hand-derived example in tests/golden/hand_worked_hsa.txt: T_r, block lists and
+    frame means, plus the attention outputs in closed form."""
+    g = _golden("hand_worked_hsa.txt")
+    d, tpf = int(g["d"][0]), int(g["tpf"][0])
+    K = np.array(g["K"]).reshape(1, 1, -1, d)
+    Q = np.array(g["Q"]).reshape(1, 1, -1, d)
+    V = np.stack([np.arange(K.shape[2], dtype=float), np.ones(K.shape[2])], axis=1)[None, None]
     c = 1 / math.sqrt(2)
-    out = oracle.hsa(Q, K, V, tpf=2, bs=1, n_kframes=4, mem=[1, 2], forced=[0, 3],
-                     k_f=1, k_b=1, scale=c)
-    assert out["frames"][0, 0].tolist() == [[0, 1, 3], [0, 2, 3]]
-    assert out["blocks"][0, 0].tolist() == [[0, 2, 6], [1, 4, 6]]
+    out = oracle.hsa(Q, K, V, tpf=tpf, bs=int(g["bs"][0]), n_kframes=int(g["n_kframes"][0]),
+                     mem=[int(x) for x in g["mem"]], forced=[int(x) for x in g["forced"]],
+                     k_f=int(g["k_f"][0]), k_b=int(g["k_b"][0]), scale=c)
+    n_q = Q.shape[2]
+    assert out["frames"][0, 0].tolist() == np.array(g["frames"], int).reshape(n_q, -1).tolist()
+    assert out["blocks"][0, 0].tolist() == np.array(g["blocks"], int).reshape(n_q, -1).tolist()
+    assert np.allclose(out["k_frm"][0, 0], np.array(g["frame_means"]).reshape(-1, d), atol=0)
     e1, e2 = math.exp(c), math.exp(2 * c)
     den = 2 * e1 + e2
     assert out["o"][0, 0, 0].tolist() == pytest.approx([(2 * e2 + 6 * e1) / den, 1.0], abs=1e-14)
     assert out["o"][0, 0, 1].tolist() == pytest.approx([(7 * e1 + 4 * e2) / den, 1.0], abs=1e-14)
-    assert np.allclose(out["k_frm"][0, 0], [[.5, .5], [1, 0], [0, 2], [0, 1]], atol=0)
 
 
 # ----------------------------------------------------------------------------- pooling
