@@ -1,113 +1,157 @@
 // Token compression by mean pooling (Light Forcing summary, execution flow, stage 2):
 // block-level means of queries and keys, frame-level means of keys.
 //
-// pool_blocks: one 256-thread workgroup per (b, h, block). The block's tokens are
-// streamed once from HBM with 16-byte loads: thread t reads chunk t % C of every
-// P-th token (C = 16-byte chunks per token, P = 256 / C token lanes), accumulating in
-// fp32; the P partial sums meet in LDS and are added in a fixed order, so results are
-// deterministic. Many small workgroups (B*H*n_frames*n_bpf) keep every CU streaming.
+// One wave pools one block at a time: lane l reads 16-byte chunk l % C of every TL-th
+// token of the block (C = 16-byte chunks per token, TL = 64 / C token lanes),
+// accumulating in fp32; the TL partial sums of each chunk are
+// added across lanes in a fixed order, and the first C lanes write the block mean (the
+// sum divided by the block's true token count). Every input byte is read once, with
+// fully coalesced loads.
 //
-// frame_means: one workgroup per (b, h, frame), d threads; weights the frame's fp32
-// block means by their token counts (the true frame mean up to fp32 rounding).
+// With frame means requested, a 1024-thread workgroup owns one whole frame: its 16
+// waves take the frame's blocks in turn, keep the running sum of their block sums, and
+// the frame mean is the sum of the waves' sums (added in a fixed order) divided by the
+// frame's token count. Without, a 256-thread workgroup owns four blocks (one per wave),
+// which keeps short tensors (the chunk's queries) spread over every CU. Each lane keeps
+// up to 16 tokens' loads in flight. Results are deterministic.
 #include "lf_device.h"
 #include "lf_kernels.h"
 
 namespace lf {
 
+constexpr int kPoolWaves = 4;        // waves per workgroup without frame means
+constexpr int kFrameWaves = 16;      // waves per workgroup owning a whole frame
+
 template <typename T>
-__device__ __forceinline__ void load16_to_f32(const T* p, float* out);
+struct Chunk16;
 
 template <>
-__device__ __forceinline__ void load16_to_f32<float>(const float* p, float* out) {
-  const float4 v = *reinterpret_cast<const float4*>(p);
-  out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
-}
-
-template <>
-__device__ __forceinline__ void load16_to_f32<__bf16>(const __bf16* p, float* out) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[2 * i] = __uint_as_float(w[i] << 16);
-    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+struct Chunk16<float> {
+  static constexpr int E = 4;  // elements per 16-byte chunk
+  __device__ static __forceinline__ void add(const float* p, float* acc) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
   }
+};
+
+template <>
+struct Chunk16<__bf16> {
+  static constexpr int E = 8;
+  __device__ static __forceinline__ void add(const __bf16* p, float* acc) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(w[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+// Sum over the TL token lanes holding the same chunk (lanes c, c + C, c + 2C, ...):
+// a butterfly over the lane bits above C, in a fixed order.
+template <int C>
+__device__ __forceinline__ float token_lane_sum(float x) {
+#pragma unroll
+  for (int m = C; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
+  return x;
 }
+
+// Sums of block j of a frame (the frame's tokens [j*bs, j*bs + len)) into `sum`,
+// valid in lanes < C (lane c holds chunk c). Up to kBatch tokens per lane are loaded
+// before any is added, so a wave keeps kBatch * 1 KB in flight.
+constexpr int kBatch = 16;
 
 template <typename T, int D>
-__global__ void __launch_bounds__(256) pool_blocks_kernel(const T* __restrict__ x,
-                                                          float* __restrict__ blk,
-                                                          int n_frames, int tpf, int bs,
-                                                          int n_bpf, long long x_stride) {
-  constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
-  constexpr int C = D / E;           // chunks per token
-  constexpr int P = 256 / C;         // tokens in flight per pass
-  __shared__ float red[P][D + 4];
-
-  const int nb = n_frames * n_bpf;
-  const int bh = blockIdx.x / nb;
-  const int gb = blockIdx.x - bh * nb;
-  const int f = gb / n_bpf, j = gb - f * n_bpf;
-  const int len = min(bs, tpf - j * bs);
-  const T* base = x + (static_cast<size_t>(bh) * x_stride + f * tpf + j * bs) * D;
-
-  const int c = threadIdx.x % C, s = threadIdx.x / C;
-  float acc[E];
+__device__ __forceinline__ void block_sum(const T* __restrict__ frame, int j, int bs, int len, int lane,
+                                          float* sum) {
+  constexpr int E = Chunk16<T>::E;
+  constexpr int C = D / E;
+  constexpr int TL = kWave / C;
+  const int c = lane % C, s = lane / C;
+  const T* base = frame + static_cast<size_t>(j) * bs * D + c * E;
+  float a[E], b[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-
-  int t = s;
-  for (; t + 3 * P < len; t += 4 * P) {  // four independent loads in flight
-    float v0[E], v1[E], v2[E], v3[E];
-    load16_to_f32<T>(base + static_cast<size_t>(t) * D + c * E, v0);
-    load16_to_f32<T>(base + static_cast<size_t>(t + P) * D + c * E, v1);
-    load16_to_f32<T>(base + static_cast<size_t>(t + 2 * P) * D + c * E, v2);
-    load16_to_f32<T>(base + static_cast<size_t>(t + 3 * P) * D + c * E, v3);
+  for (int e = 0; e < E; ++e) a[e] = b[e] = 0.f;
+  for (int t0 = 0; t0 < len; t0 += kBatch * TL) {
+    uint4 v[kBatch];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += ((v0[e] + v1[e]) + (v2[e] + v3[e]));
-  }
-  for (; t < len; t += P) {
-    float v0[E];
-    load16_to_f32<T>(base + static_cast<size_t>(t) * D + c * E, v0);
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + s + u * TL;
+      v[u] = t < len ? *reinterpret_cast<const uint4*>(base + static_cast<size_t>(t) * D) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += v0[e];
+    for (int u = 0; u < kBatch; ++u) Chunk16<T>::add(reinterpret_cast<const T*>(&v[u]), (u & 1) ? b : a);
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[s][c * E + e] = acc[e];
-  __syncthreads();
-
-  const float inv = 1.0f / static_cast<float>(len);
-  for (int i = threadIdx.x; i < D; i += 256) {
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < P; ++r) sum += red[r][i];
-    blk[(static_cast<size_t>(bh) * nb + gb) * D + i] = sum * inv;
-  }
+  for (int e = 0; e < E; ++e) sum[e] = token_lane_sum<C>(a[e] + b[e]);
 }
 
-template <int D>
-__global__ void __launch_bounds__(D) frame_means_kernel(const float* __restrict__ blk,
-                                                        float* __restrict__ frm, int n_frames,
-                                                        int tpf, int bs, int n_bpf) {
-  const int bh = blockIdx.x / n_frames;
-  const int f = blockIdx.x - bh * n_frames;
-  const float* b = blk + (static_cast<size_t>(bh) * n_frames + f) * n_bpf * D + threadIdx.x;
-  float sum = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < n_bpf; ++j) sum = fmaf(b[j * D], static_cast<float>(min(bs, tpf - j * bs)), sum);
-  frm[(static_cast<size_t>(bh) * n_frames + f) * D + threadIdx.x] = sum / static_cast<float>(tpf);
+// FRAMES: one workgroup per (b, h, frame), writing block and frame means. Otherwise one
+// workgroup per (b, h, frame, group of kPoolWaves blocks), block means only.
+template <typename T, int D, bool FRAMES>
+__global__ void __launch_bounds__((FRAMES ? kFrameWaves : kPoolWaves) * kWave) pool_kernel(const T* __restrict__ x, float* __restrict__ blk,
+                                                                  float* __restrict__ frm, int n_frames, int tpf,
+                                                                  int bs, int n_bpf, long long x_stride) {
+  constexpr int E = Chunk16<T>::E;
+  constexpr int C = D / E;
+  constexpr int W = FRAMES ? kFrameWaves : kPoolWaves;
+  __shared__ __attribute__((aligned(16))) float fs[W][D];
+  const int groups = FRAMES ? 1 : (n_bpf + kPoolWaves - 1) / kPoolWaves;
+  const int grp = blockIdx.x % groups;
+  const int bf = blockIdx.x / groups;                 // bh * n_frames + f
+  const int bh = bf / n_frames, f = bf - bh * n_frames;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const T* frame = x + (static_cast<size_t>(bh) * x_stride + static_cast<size_t>(f) * tpf) * D;
+  float* blk_row = blk + static_cast<size_t>(bf) * n_bpf * D;
+
+  float fsum[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) fsum[e] = 0.f;
+  const int j0 = FRAMES ? wave : grp * kPoolWaves + wave;
+  const int dj = FRAMES ? kFrameWaves : n_bpf;     // without frames: one block per wave
+  for (int j = j0; j < n_bpf; j += dj) {
+    const int len = min(bs, tpf - j * bs);
+    float sum[E];
+    block_sum<T, D>(frame, j, bs, len, lane, sum);
+    if (lane < C) {
+      const float inv = 1.0f / static_cast<float>(len);
+      float* out = blk_row + static_cast<size_t>(j) * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4*>(out + e) =
+            make_float4(sum[e] * inv, sum[e + 1] * inv, sum[e + 2] * inv, sum[e + 3] * inv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) fsum[e] += sum[e];
+    }
+  }
+  if (!FRAMES) return;
+  if (lane < C) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) fs[wave][lane * E + e] = fsum[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) t += fs[w][threadIdx.x];
+    frm[static_cast<size_t>(bf) * D + threadIdx.x] = t / static_cast<float>(tpf);
+  }
 }
 
 template <typename T, int D>
 static hipError_t launch_pool_t(const void* x, int BH, int n_frames, int tpf, int bs, int n_bpf,
                                 long long x_stride, float* blk, float* frm, hipStream_t st) {
-  const unsigned nblk = static_cast<unsigned>(BH) * n_frames * n_bpf;
-  hipLaunchKernelGGL((pool_blocks_kernel<T, D>), dim3(nblk), dim3(256), 0, st,
-                     static_cast<const T*>(x), blk, n_frames, tpf, bs, n_bpf, x_stride);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || frm == nullptr) return e;
-  hipLaunchKernelGGL((frame_means_kernel<D>), dim3(static_cast<unsigned>(BH) * n_frames), dim3(D),
-                     0, st, blk, frm, n_frames, tpf, bs, n_bpf);
+  const unsigned frames = static_cast<unsigned>(BH) * n_frames;
+  const dim3 block(kPoolWaves * kWave);
+  if (frm != nullptr) {
+    hipLaunchKernelGGL((pool_kernel<T, D, true>), dim3(frames), dim3(kFrameWaves * kWave), 0, st, static_cast<const T*>(x), blk, frm,
+                       n_frames, tpf, bs, n_bpf, x_stride);
+  } else {
+    const unsigned groups = (n_bpf + kPoolWaves - 1) / kPoolWaves;
+    hipLaunchKernelGGL((pool_kernel<T, D, false>), dim3(frames * groups), block, 0, st, static_cast<const T*>(x),
+                       blk, frm, n_frames, tpf, bs, n_bpf, x_stride);
+  }
   return hipGetLastError();
 }
 
