@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 import sparse_attention_autoregressive_amd as lf  # noqa: E402
+from sparse_attention_autoregressive_amd.profsum import read_traffic  # noqa: E402
 from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, SweepWorkspace, Workspace,  # noqa: E402
                                                           attend, plan_sweep, pool_k, pool_q, select,
                                                           sweep_layer)
@@ -95,6 +96,14 @@ def run_cpu_baseline(w, k_b: int, heads: int, min_s: float):
         reps += 1
     dense, _ = flops_of(ws, out["blocks"])
     return dense * reps / dt / 1e12, dt, reps, dense
+
+
+def traffic_of(workload: str):
+    """HBM bytes per attention launch from the committed counter summary of this workload
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None when there is
+    none or it was taken on a different version of the kernel source."""
+    got = read_traffic(os.path.join(ROOT, "profiles", f"attn_bf16_{workload}_hbm_traffic.md"))
+    return None if got is None else got[0]
 
 
 def hold_stream(ms: float = 50.0):
@@ -264,7 +273,8 @@ def main():
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
         "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_of(w.name)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
@@ -376,7 +386,7 @@ def bench_sweep(args):
         "chunk_us_per_sweep": [round(x, 1) for x in chunk_us],
         "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": traffic_of(s.name)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
