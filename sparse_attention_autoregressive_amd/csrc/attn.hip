@@ -198,11 +198,15 @@ __device__ __forceinline__ void tile_compute(const lds_u8* Kt, const lds_u8* Vt,
   f32x16 sacc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+  // wave priority is raised while this wave issues matrix-core work, so a SIMD's other
+  // wave, busy with its softmax, yields issue slots to it and the matrix core stays fed
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int st = 0; st < KS; ++st) {
     const bf16x8 kf = *reinterpret_cast<lds_bf16x8*>(Kt + s.k_off[st]);
     sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, s.qf[st], sacc, 0, 0, 0);
   }
+  __builtin_amdgcn_s_setprio(0);
   // V^T fragments, in flight while the softmax runs; rows 16ks + 8h of the lane's column
   bf16x8 vf[DT][2];
 #pragma unroll
@@ -253,6 +257,7 @@ __device__ __forceinline__ void tile_compute(const lds_u8* Kt, const lds_u8* Vt,
   }
   const u32x4 plo = {pw[0], pw[1], pw[2], pw[3]}, phi = {pw[4], pw[5], pw[6], pw[7]};
   const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, plo), __builtin_bit_cast(bf16x8, phi)};
+  __builtin_amdgcn_s_setprio(1);
   // O^T += V^T P^T; the two transposing reads give this lane's d the same keys
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -267,6 +272,7 @@ __device__ __forceinline__ void tile_compute(const lds_u8* Kt, const lds_u8* Vt,
   // lane l receives (4(l/16) .. +3 of column l%16) all hold the sum of query l%32.
   s.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.sum_sel, pb[0], s.lsum, 0, 0, 0);
   s.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.sum_sel, pb[1], s.lsum, 0, 0, 0);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D>
