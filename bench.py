@@ -1,9 +1,9 @@
 """Benchmark of the HSA hot path on one MI355X.
 
 One step = one chunk of one layer through the whole path: the CAG schedule and block
-budget on the host, then pool Q, pool K (block + frame means), selection (frame top-k and
-block top-k in one launch) and block-sparse attention on the GPU, each a C-ABI call on
-torch's current stream.
+budget on the host, then pooling (query block means, key block and frame means: one
+launch), selection (frame top-k and block top-k: one launch) and block-sparse attention
+on the GPU, each a C-ABI call on torch's current stream.
 Default workload: the 480p layer at chunk 2 of 7 (12 heads x 128, 4680 query tokens
 against 6 frames = 9360 key tokens, 64-token blocks, CAG sparsity s_2 -> 6 frames x 6
 blocks per row); --workload selects the chunk-7 layer, the 69-frame long-memory layer,
@@ -37,13 +37,12 @@ import synth  # noqa: E402
 import sparse_attention_autoregressive_amd as lf  # noqa: E402
 from sparse_attention_autoregressive_amd.profsum import read_traffic  # noqa: E402
 from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, SweepWorkspace, Workspace,  # noqa: E402
-                                                          attend, plan_sweep, pool_k, pool_q, select,
-                                                          sweep_layer)
+                                                          attend, plan_sweep, pool, select, sweep_layer)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "HSA effective TFLOP/s (dense-equiv) + % MFMA peak + select overhead %, 480p"
-KERNELS = ["pool_q", "pool_k", "select", "attn"]
+KERNELS = ["pool", "select", "attn"]
 
 
 def chunk_flops(w):
@@ -183,8 +182,7 @@ def main():
         lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
         ws = wss[i % len(sets)]
         q, k, v = sets[i % len(sets)]
-        calls = [lambda: pool_q(ws, q), lambda: pool_k(ws, k), lambda: select(ws),
-                 lambda: attend(ws, q, k, v)]
+        calls = [lambda: pool(ws, q, k), lambda: select(ws), lambda: attend(ws, q, k, v)]
         for j, c in enumerate(calls):
             if ev is not None:
                 ev[j].record(stream)
@@ -219,21 +217,19 @@ def main():
 
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
-    t_attn = mean_us[3] * 1e-6
+    t_attn = mean_us[2] * 1e-6
     t_path = mean_us.sum() * 1e-6
     attn_tflops = f_active / t_attn / 1e12
     value = f_dense / (ms_per_step * 1e-3) / 1e12
-    sel_pct = 100.0 * mean_us[2] / mean_us[3]
-    pool_gbs = {
-        "pool_q": pool_bytes(w, w.n_qframes, False) / (mean_us[0] * 1e-6) / 1e9,
-        "pool_k": pool_bytes(w, w.n_kframes, True) / (mean_us[1] * 1e-6) / 1e9,
-    }
+    sel_pct = 100.0 * mean_us[1] / mean_us[2]
+    pool_gbs = {"pool": (pool_bytes(w, w.n_qframes, False) + pool_bytes(w, w.n_kframes, True))
+                        / (mean_us[0] * 1e-6) / 1e9}
     n_rows = w.B * w.H * plan.n_qb
     # algorithmic HBM bytes of the selection launch: q~ rows, each head's frame means and
     # block means once (they stay in L2 across the head's rows), T_r and list writes
     sel_bytes = (n_rows * (w.d * 4 + plan.W_f * 4 + plan.W_b * 4)
                  + w.B * w.H * w.n_kframes * (nb + 1) * w.d * 4)
-    sel_gbs = {"select": sel_bytes / (mean_us[2] * 1e-6) / 1e9}
+    sel_gbs = {"select": sel_bytes / (mean_us[1] * 1e-6) / 1e9}
 
     cpu = None
     if args.cpu_heads > 0:
@@ -264,7 +260,7 @@ def main():
                    "cag_beta": beta, "input_sets": len(sets)},
         "mfma_pct_peak_active": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
         "select_overhead_pct": sel_pct,
-        "pool_select_pct_of_attn": 100.0 * (mean_us[:3].sum()) / mean_us[3],
+        "pool_select_pct_of_attn": 100.0 * (mean_us[:2].sum()) / mean_us[2],
         "dense_equiv_tflops_attn_only": f_dense / t_attn / 1e12,
         "dense_equiv_tflops_kernel_sum": f_dense / t_path / 1e12,
         "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
@@ -280,7 +276,7 @@ def main():
     print(json.dumps(line))
 
 
-STAGES = ["pool_q", "pool_k", "select", "attn"]
+STAGES = ["pool", "select", "attn"]
 
 
 def bench_sweep(args):

@@ -119,6 +119,20 @@ lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float
                   float* frm_out, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * lf_pool_qk -- [S2] both poolings of one chunk in one launch: the chunk's queries (block
+ * means only) and all keys (block and frame means), with results bitwise equal to
+ * lf_pool(q, ..., n_qframes, q_blk, NULL) followed by lf_pool(k, ..., n_kframes, k_blk,
+ * k_frm).
+ * q: [B, H, n_qframes*tpf, d], k: [B, H, n_kframes*tpf, d], both in dtype dt; a nonzero
+ *   g.head_stride applies to both (>= both token counts), 0 means each is packed.
+ * q_blk: [B, H, n_qframes*n_bpf, d] fp32; k_blk: [B, H, n_kframes*n_bpf, d] fp32;
+ *   k_frm: [B, H, n_kframes, d] fp32.
+ * Limits and errors: those of lf_pool.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32_t n_qframes,
+                     int32_t n_kframes, float* q_blk, float* k_blk, float* k_frm, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * lf_select_frames -- [S3] frame stage: for every row (b, h, query block r), the frame
  * relevance p_r(f) = <q~_r, k^_f> over the memory set M; the top-min(k_f, |M|)
  * frames of M ranked by (score descending, frame id ascending) join the always-kept

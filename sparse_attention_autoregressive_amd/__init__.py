@@ -78,6 +78,7 @@ def _load():
         "lf_cag_schedule": [i32, i32, f64, f64, pf64, pf64, pf64, pf64],
         "lf_block_budget": [f64, i32, i32, i32, pi32],
         "lf_pool": [vp, i32, Geom, i32, vp, vp, vp],
+        "lf_pool_qk": [vp, vp, i32, Geom, i32, i32, vp, vp, vp, vp],
         "lf_select_frames": [vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, vp, vp],
         "lf_select_blocks": [vp, vp, Geom, i32, i32, vp, i32, i32, vp, vp],
         "lf_select": [vp, vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, i32, vp, vp, vp],
@@ -176,6 +177,29 @@ def lf_pool(x: torch.Tensor, g: Geom, n_frames: int, blk_out: Optional[torch.Ten
     _check(lib.lf_pool(x.data_ptr(), _dtype_code(x), gx, n_frames, _dev(blk_out, "blk_out"),
                        None if frm_out is None else _dev(frm_out, "frm_out"), _stream(x)))
     return blk_out, frm_out
+
+
+def lf_pool_qk(q: torch.Tensor, k: torch.Tensor, g: Geom, n_qframes: int, n_kframes: int,
+               q_blk: Optional[torch.Tensor] = None, k_blk: Optional[torch.Tensor] = None,
+               k_frm: Optional[torch.Tensor] = None):
+    """Query block means and key block + frame means in one launch: (q_blk, k_blk, k_frm)."""
+    lib = _load()
+    nb = n_bpf(g)
+    f32, dev = torch.float32, q.device
+    if q_blk is None:
+        q_blk = torch.empty((g.B, g.H, n_qframes * nb, g.d), dtype=f32, device=dev)
+    if k_blk is None:
+        k_blk = torch.empty((g.B, g.H, n_kframes * nb, g.d), dtype=f32, device=dev)
+    if k_frm is None:
+        k_frm = torch.empty((g.B, g.H, n_kframes, g.d), dtype=f32, device=dev)
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    lq, lk = n_qframes * g.tokens_per_frame, n_kframes * g.tokens_per_frame
+    strides = [_tokens(q, "q", g, lq), _tokens(k, "k", g, lk)]
+    gg = g.with_stride(0) if strides == [lq, lk] else _common_stride(g, strides)
+    _check(lib.lf_pool_qk(q.data_ptr(), k.data_ptr(), _dtype_code(q), gg, n_qframes, n_kframes,
+                          _dev(q_blk, "q_blk"), _dev(k_blk, "k_blk"), _dev(k_frm, "k_frm"), _stream(q)))
+    return q_blk, k_blk, k_frm
 
 
 def lf_select_frames(q_blk: torch.Tensor, k_frm: torch.Tensor, g: Geom, n_qb: int, n_kframes: int,

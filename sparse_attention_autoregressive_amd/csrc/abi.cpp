@@ -207,6 +207,33 @@ lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float
                     fn);
 }
 
+lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32_t n_qframes,
+                     int32_t n_kframes, float* q_blk, float* k_blk, float* k_frm, void* stream) {
+  const char* fn = "lf_pool_qk";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (dt != LF_FP32 && dt != LF_BF16) return fail(LF_ERR_UNSUPPORTED, "%s: dtype %d unsupported", fn, (int)dt);
+  if (n_qframes < 1 || n_kframes < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_qframes and n_kframes must be >= 1", fn);
+  if (!q || !k || !q_blk || !k_blk || !k_frm) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_blk) || !aligned16(k_blk) || !aligned16(k_frm))
+    return fail(LF_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const int n_bpf = n_bpf_of(g);
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  const long long lq = static_cast<long long>(n_qframes) * g.tokens_per_frame;
+  const long long lk = static_cast<long long>(n_kframes) * g.tokens_per_frame;
+  if (!fits_int(BH * n_kframes * n_bpf) || !fits_int(BH * n_qframes * n_bpf + BH * n_kframes) ||
+      !fits_int(lq) || !fits_int(lk))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  if (g.head_stride != 0 && (g.head_stride < lq || g.head_stride < lk))
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d is below the query or key token count", fn,
+                g.head_stride);
+  pending_error();
+  return hip_status(lf::launch_pool_qk(q, k, dt == LF_BF16, g.d, static_cast<int>(BH), n_qframes, n_kframes,
+                                       g.tokens_per_frame, g.block_size, n_bpf, g.head_stride ? g.head_stride : lq,
+                                       g.head_stride ? g.head_stride : lk, q_blk, k_blk, k_frm,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
                            int32_t n_kframes, const int32_t* mem, int32_t n_mem,
                            const int32_t* forced, int32_t n_forced, int32_t k_f,

@@ -18,6 +18,12 @@ struct FrameLists {
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
                        int n_bpf, long long x_stride, float* blk, float* frm, hipStream_t st);
 
+// Queries (block means) and keys (block and frame means) in one launch; q_stride and
+// k_stride: tokens between consecutive (b, h) slices of q and k.
+hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH, int n_qframes, int n_kframes,
+                          int tpf, int bs, int n_bpf, long long q_stride, long long k_stride, float* q_blk,
+                          float* k_blk, float* k_frm, hipStream_t st);
+
 // One launch of the selection kernel over n_rows = B*H*n_qb rows. Frame stage: reads
 // q_blk, k_frm, lists, n_mem, n_forced, k_eff and writes frames_out (if set). Block
 // stage: reads q_blk, k_blk and the frame lists (from the frame stage, else frames_in)

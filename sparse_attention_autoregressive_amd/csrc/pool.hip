@@ -13,7 +13,10 @@
 // the frame mean is the sum of the waves' sums (added in a fixed order) divided by the
 // frame's token count. Without, a 256-thread workgroup owns four blocks (one per wave),
 // which keeps short tensors (the chunk's queries) spread over every CU. Each lane keeps
-// up to 16 tokens' loads in flight. Results are deterministic.
+// up to 16 tokens' loads in flight. A combined launch pools a chunk's queries and all
+// keys together (16 query blocks per workgroup); every block is summed by one wave with
+// the same code either way, so results match the separate launches bitwise. Results
+// are deterministic.
 #include "lf_device.h"
 #include "lf_kernels.h"
 
@@ -87,19 +90,18 @@ __device__ __forceinline__ void block_sum(const T* __restrict__ frame, int j, in
   for (int e = 0; e < E; ++e) sum[e] = token_lane_sum<C>(a[e] + b[e]);
 }
 
-// FRAMES: one workgroup per (b, h, frame), writing block and frame means. Otherwise one
-// workgroup per (b, h, frame, group of kPoolWaves blocks), block means only.
-template <typename T, int D, bool FRAMES>
-__global__ void __launch_bounds__((FRAMES ? kFrameWaves : kPoolWaves) * kWave) pool_kernel(const T* __restrict__ x, float* __restrict__ blk,
-                                                                  float* __restrict__ frm, int n_frames, int tpf,
-                                                                  int bs, int n_bpf, long long x_stride) {
+// The work of workgroup `wg` (W waves). FRAMES: one workgroup per (b, h, frame), writing
+// block and frame means. Otherwise one workgroup per (b, h, frame, group of W blocks),
+// block means only.
+template <typename T, int D, bool FRAMES, int W>
+__device__ __forceinline__ void pool_part(const T* __restrict__ x, float* __restrict__ blk, float* __restrict__ frm,
+                                          int n_frames, int tpf, int bs, int n_bpf, long long x_stride, int wg,
+                                          float (*fs)[D]) {
   constexpr int E = Chunk16<T>::E;
   constexpr int C = D / E;
-  constexpr int W = FRAMES ? kFrameWaves : kPoolWaves;
-  __shared__ __attribute__((aligned(16))) float fs[W][D];
-  const int groups = FRAMES ? 1 : (n_bpf + kPoolWaves - 1) / kPoolWaves;
-  const int grp = blockIdx.x % groups;
-  const int bf = blockIdx.x / groups;                 // bh * n_frames + f
+  const int groups = FRAMES ? 1 : (n_bpf + W - 1) / W;
+  const int grp = wg % groups;
+  const int bf = wg / groups;                         // bh * n_frames + f
   const int bh = bf / n_frames, f = bf - bh * n_frames;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const T* frame = x + (static_cast<size_t>(bh) * x_stride + static_cast<size_t>(f) * tpf) * D;
@@ -108,8 +110,8 @@ __global__ void __launch_bounds__((FRAMES ? kFrameWaves : kPoolWaves) * kWave) p
   float fsum[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) fsum[e] = 0.f;
-  const int j0 = FRAMES ? wave : grp * kPoolWaves + wave;
-  const int dj = FRAMES ? kFrameWaves : n_bpf;     // without frames: one block per wave
+  const int j0 = FRAMES ? wave : grp * W + wave;
+  const int dj = FRAMES ? W : n_bpf;               // without frames: one block per wave
   for (int j = j0; j < n_bpf; j += dj) {
     const int len = min(bs, tpf - j * bs);
     float sum[E];
@@ -139,20 +141,70 @@ __global__ void __launch_bounds__((FRAMES ? kFrameWaves : kPoolWaves) * kWave) p
   }
 }
 
+template <typename T, int D, bool FRAMES>
+__global__ void __launch_bounds__((FRAMES ? kFrameWaves : kPoolWaves) * kWave) pool_kernel(
+    const T* __restrict__ x, float* __restrict__ blk, float* __restrict__ frm, int n_frames, int tpf, int bs,
+    int n_bpf, long long x_stride) {
+  constexpr int W = FRAMES ? kFrameWaves : kPoolWaves;
+  __shared__ __attribute__((aligned(16))) float fs[W][D];
+  pool_part<T, D, FRAMES, W>(x, blk, frm, n_frames, tpf, bs, n_bpf, x_stride, blockIdx.x, fs);
+}
+
+// Queries (block means) and keys (block and frame means) in one launch: the first n_qwg
+// workgroups pool query blocks, 16 per workgroup, the rest one key frame each.
+template <typename T, int D>
+__global__ void __launch_bounds__(kFrameWaves * kWave) pool_qk_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ q_blk, float* __restrict__ k_blk,
+    float* __restrict__ k_frm, int n_qframes, int n_kframes, int tpf, int bs, int n_bpf, long long q_stride,
+    long long k_stride, int n_qwg) {
+  __shared__ __attribute__((aligned(16))) float fs[kFrameWaves][D];
+  const int wg = blockIdx.x;
+  if (wg < n_qwg)
+    pool_part<T, D, false, kFrameWaves>(q, q_blk, nullptr, n_qframes, tpf, bs, n_bpf, q_stride, wg, fs);
+  else
+    pool_part<T, D, true, kFrameWaves>(k, k_blk, k_frm, n_kframes, tpf, bs, n_bpf, k_stride, wg - n_qwg, fs);
+}
+
 template <typename T, int D>
 static hipError_t launch_pool_t(const void* x, int BH, int n_frames, int tpf, int bs, int n_bpf,
                                 long long x_stride, float* blk, float* frm, hipStream_t st) {
   const unsigned frames = static_cast<unsigned>(BH) * n_frames;
-  const dim3 block(kPoolWaves * kWave);
   if (frm != nullptr) {
-    hipLaunchKernelGGL((pool_kernel<T, D, true>), dim3(frames), dim3(kFrameWaves * kWave), 0, st, static_cast<const T*>(x), blk, frm,
-                       n_frames, tpf, bs, n_bpf, x_stride);
+    hipLaunchKernelGGL((pool_kernel<T, D, true>), dim3(frames), dim3(kFrameWaves * kWave), 0, st,
+                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride);
   } else {
     const unsigned groups = (n_bpf + kPoolWaves - 1) / kPoolWaves;
-    hipLaunchKernelGGL((pool_kernel<T, D, false>), dim3(frames * groups), block, 0, st, static_cast<const T*>(x),
-                       blk, frm, n_frames, tpf, bs, n_bpf, x_stride);
+    hipLaunchKernelGGL((pool_kernel<T, D, false>), dim3(frames * groups), dim3(kPoolWaves * kWave), 0, st,
+                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_pool_qk_t(const void* q, const void* k, int BH, int n_qframes, int n_kframes, int tpf,
+                                   int bs, int n_bpf, long long q_stride, long long k_stride, float* q_blk,
+                                   float* k_blk, float* k_frm, hipStream_t st) {
+  const int n_qwg = BH * n_qframes * ((n_bpf + kFrameWaves - 1) / kFrameWaves);
+  const unsigned grid = static_cast<unsigned>(n_qwg) + static_cast<unsigned>(BH) * n_kframes;
+  hipLaunchKernelGGL((pool_qk_kernel<T, D>), dim3(grid), dim3(kFrameWaves * kWave), 0, st,
+                     static_cast<const T*>(q), static_cast<const T*>(k), q_blk, k_blk, k_frm, n_qframes, n_kframes,
+                     tpf, bs, n_bpf, q_stride, k_stride, n_qwg);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH, int n_qframes, int n_kframes,
+                          int tpf, int bs, int n_bpf, long long q_stride, long long k_stride, float* q_blk,
+                          float* k_blk, float* k_frm, hipStream_t st) {
+  if (bf16) {
+    return d == 128 ? launch_pool_qk_t<__bf16, 128>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
+                                                    k_stride, q_blk, k_blk, k_frm, st)
+                    : launch_pool_qk_t<__bf16, 64>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
+                                                   k_stride, q_blk, k_blk, k_frm, st);
+  }
+  return d == 128 ? launch_pool_qk_t<float, 128>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
+                                                 k_stride, q_blk, k_blk, k_frm, st)
+                  : launch_pool_qk_t<float, 64>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride, k_stride,
+                                                q_blk, k_blk, k_frm, st);
 }
 
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,

@@ -3,7 +3,7 @@
 Order (Light Forcing summary, execution flow, stages 2-3): pool the chunk's queries
 (block means q~), pool all keys (block means k~ and frame means k^), frame top-k per
 query block (T_r) and block top-k inside the chosen frames (the mask B_r as id lists)
-in one selection launch, block-sparse attention. All outputs are allocated once in a `Workspace`, so repeated
+in one selection launch, block-sparse attention. The two poolings share one launch. All outputs are allocated once in a `Workspace`, so repeated
 calls (timing loops, the per-layer sweep) allocate nothing.
 """
 from __future__ import annotations
@@ -13,7 +13,7 @@ from typing import List, Sequence
 
 import torch
 
-from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_select, lf_select_blocks,
+from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_pool_qk, lf_select, lf_select_blocks,
                lf_select_frames, lf_sparse_attn, n_bpf)
 
 
@@ -74,6 +74,12 @@ def pool_k(ws: Workspace, k: torch.Tensor):
     lf_pool(k, p.geom, p.n_kframes, blk_out=ws.k_blk, frm_out=ws.k_frm)
 
 
+def pool(ws: Workspace, q: torch.Tensor, k: torch.Tensor):
+    """Both poolings in one launch (same results as pool_q + pool_k)."""
+    p = ws.plan
+    lf_pool_qk(q, k, p.geom, p.n_qframes, p.n_kframes, ws.q_blk, ws.k_blk, ws.k_frm)
+
+
 def select_frames(ws: Workspace):
     p = ws.plan
     lf_select_frames(ws.q_blk, ws.k_frm, p.geom, p.n_qb, p.n_kframes, p.mem, p.forced, p.k_f,
@@ -101,8 +107,7 @@ def attend(ws: Workspace, q, k, v, out=None):
 def hsa_chunk(ws: Workspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out=None) -> torch.Tensor:
     """Pool, select and attend for one chunk; returns the output (enqueued on the current
     stream). q, k, v and out may be token-range views of bigger per-head allocations."""
-    pool_q(ws, q)
-    pool_k(ws, k)
+    pool(ws, q, k)
     select(ws)
     attend(ws, q, k, v, out)
     return ws.o if out is None else out
@@ -174,7 +179,7 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
     """All chunks of one layer in order. q, k, v, o: [B, H, n_frames*tpf, d] holding the
     whole clip; chunk i reads its query frames and the key prefix as views and writes its
     frames of o. Enqueued on the current stream; returns o. `mark(i, stage)`, if given,
-    is called before each stage ("pool_q", "pool_k", "select", "attn") and with stage
+    is called before each stage ("pool", "select", "attn") and with stage
     "end" after chunk i (e.g. to record timing events)."""
     sp = sw.plan
     tpf = sp.geom.tokens_per_frame
@@ -186,10 +191,8 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
             tick(i, "attn")
             lf_sparse_attn(qv, kv, vv, p.geom, p.n_qframes, p.n_kframes, sw.full[i], p.scale, out=ov)
         else:
-            tick(i, "pool_q")
-            pool_q(ws, qv)
-            tick(i, "pool_k")
-            pool_k(ws, kv)
+            tick(i, "pool")
+            pool(ws, qv, kv)
             tick(i, "select")
             select(ws)
             tick(i, "attn")

@@ -25,7 +25,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(lf.library_path())
     names = _declared()
-    assert {"lf_pool", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
+    assert {"lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
             "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -174,6 +174,17 @@ def test_sparse_attn_validation():
     _err(c.lf_sparse_attn(F, F, F, F, 3, g, 3, 21, F, 64, 0.1, None), lf.LF_ERR_UNSUPPORTED)
     _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 80, 1560, 64), 3, 21, F, 64, 0.1, None),
          lf.LF_ERR_UNSUPPORTED)
+
+
+def test_pool_qk_validation():
+    c = _c()
+    F = FAKE
+    g = lf.Geom(1, 2, 128, 1560, 64)
+    _err(c.lf_pool_qk(F, F, 1, g, 0, 21, F, F, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool_qk(F, None, 1, g, 3, 21, F, F, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool_qk(F, F, 1, g, 3, 21, F, F, F + 4, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool_qk(F, F, 7, g, 3, 21, F, F, F, None), lf.LF_ERR_UNSUPPORTED)
+    _err(c.lf_pool_qk(F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 4680), 3, 21, F, F, F, None), lf.LF_ERR_INVALID_ARG)
 
 
 def test_head_stride_validation():

@@ -224,3 +224,19 @@ def test_select_blocks_malformed_frames_stay_in_bounds():
     torch.cuda.synchronize()
     b = blocks.cpu().numpy()
     assert b.min() >= 0 and b.max() < w.n_kframes * nb
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "480p_chunk2of7"])
+def test_pool_qk_equals_separate_pools(name):
+    """The combined query + key pooling launch (the pipeline's) gives bitwise the block and
+    frame means of two lf_pool calls."""
+    w, x, _, gpu, _, k_b = _case(name)
+    dev = torch.device("cuda")
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    q, k = x.q.to(dev), x.k.to(dev)
+    q_blk, _ = lf.lf_pool(q, g, w.n_qframes, with_frames=False)
+    k_blk, k_frm = lf.lf_pool(k, g, w.n_kframes)
+    q2, k2, f2 = lf.lf_pool_qk(q, k, g, w.n_qframes, w.n_kframes)
+    torch.cuda.synchronize()
+    assert torch.equal(q_blk, q2) and torch.equal(k_blk, k2) and torch.equal(k_frm, f2)
+    assert np.array_equal(q2.cpu().numpy(), gpu["q_blk"]) and np.array_equal(f2.cpu().numpy(), gpu["k_frm"])
