@@ -36,8 +36,9 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 import sparse_attention_autoregressive_amd as lf  # noqa: E402
 from sparse_attention_autoregressive_amd.profsum import read_traffic  # noqa: E402
-from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, SweepWorkspace, Workspace,  # noqa: E402
-                                                          attend, plan_sweep, pool, select, sweep_layer)
+from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, PooledKeyCache, SweepWorkspace,  # noqa: E402
+                                                          Workspace, attend, new_frames, plan_sweep, pool,
+                                                          pool_cached, select, select_cached, sweep_layer)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
@@ -177,43 +178,55 @@ def main():
         del src, dst
 
     stream = torch.cuda.current_stream()
+    # steady state: the history frames' pooled keys sit in a per-layer cache (filled here,
+    # before timing); a step pools the queries and the chunk's own key frames only
+    f0 = new_frames(plan)
+    caches = [PooledKeyCache(g, w.n_kframes, dev) for _ in sets]
+    for c, (_, k, _) in zip(caches, sets):
+        lf.lf_pool(k[:, :, :f0 * w.tpf], g, f0, blk_out=c.blk(0, f0), frm_out=c.frm(0, f0))
 
-    def step(i, ev=None):
+    def step(i, ev=None, cached=False):
         lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
         ws = wss[i % len(sets)]
         q, k, v = sets[i % len(sets)]
-        calls = [lambda: pool(ws, q, k), lambda: select(ws), lambda: attend(ws, q, k, v)]
-        for j, c in enumerate(calls):
+        if cached:
+            c = caches[i % len(sets)]
+            calls = [lambda: pool_cached(ws, c, q, k), lambda: select_cached(ws, c), lambda: attend(ws, q, k, v)]
+        else:
+            calls = [lambda: pool(ws, q, k), lambda: select(ws), lambda: attend(ws, q, k, v)]
+        for j, c_ in enumerate(calls):
             if ev is not None:
                 ev[j].record(stream)
-            c()
+            c_()
         if ev is not None:
             ev[len(calls)].record(stream)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def timed(cached):
+        """(ms per step by wall clock, per-call mean us, per-call median us)."""
+        print(f"[bench] warmup {args.warmup}" + (" (steady state)" if cached else ""), file=sys.stderr, flush=True)
+        for i in range(args.warmup):
+            step(i, cached=cached)
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} steps" + (" (steady state)" if cached else ""), file=sys.stderr,
+              flush=True)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, cached=cached)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # per-call times: the same steps again with events between calls, all enqueued while
+        # a spin kernel holds the stream, so host launch gaps do not show up as kernel time
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+        hold_stream()
+        for i in range(args.steps):
+            step(i, evs[i], cached=cached)
+        torch.cuda.synchronize()
+        per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(KERNELS))]
+                        for i in range(args.steps)]) * 1e3                      # us
+        return wall * 1e3 / args.steps, per.mean(axis=0), np.median(per, axis=0)
 
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # per-call times: the same steps again with events between calls, all enqueued while
-    # a spin kernel holds the stream, so host launch gaps do not show up as kernel time
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
-    hold_stream()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(KERNELS))]
-                    for i in range(args.steps)]) * 1e3                      # us
-    mean_us = per.mean(axis=0)
-    med_us = np.median(per, axis=0)
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step, mean_us, med_us = timed(False)
+    ss_ms, ss_mean, ss_med = timed(True)
 
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
@@ -230,6 +243,19 @@ def main():
     sel_bytes = (n_rows * (w.d * 4 + plan.W_f * 4 + plan.W_b * 4)
                  + w.B * w.H * w.n_kframes * (nb + 1) * w.d * 4)
     sel_gbs = {"select": sel_bytes / (mean_us[1] * 1e-6) / 1e9}
+    steady = {
+        "what": (f"history pooled keys ({f0} frames) from a per-layer cache filled before timing; a step pools "
+                 f"the queries and the chunk's own {w.n_kframes - f0} key frames, selects over the cache "
+                 f"and attends"),
+        "value": f_dense / (ss_ms * 1e-3) / 1e12,
+        "ms_per_step": ss_ms,
+        "kernel_us_mean": dict(zip(KERNELS, [round(float(x), 2) for x in ss_mean])),
+        "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in ss_med])),
+        "pool_select_pct_of_attn": 100.0 * ss_mean[:2].sum() / ss_mean[2],
+        "dense_equiv_tflops_kernel_sum": f_dense / (ss_mean.sum() * 1e-6) / 1e12,
+        "pool_gbs": round((pool_bytes(w, w.n_qframes, False) + pool_bytes(w, w.n_kframes - f0, True))
+                          / (ss_mean[0] * 1e-6) / 1e9, 1),
+    }
 
     cpu = None
     if args.cpu_heads > 0:
@@ -267,6 +293,7 @@ def main():
         "kernel_us_mean": dict(zip(KERNELS, [round(float(x), 2) for x in mean_us])),
         "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in med_us])),
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
+        "steady_state": steady,
         "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
@@ -309,41 +336,50 @@ def bench_sweep(args):
             f_dense += fd
             f_active += fa
 
-    def run(events=None):
-        for q, k, v in layers:
+    # steady state: one pooled-key cache per layer; each chunk pools only its own key frames
+    caches = [PooledKeyCache(g, sp.n_frames, dev) for _ in layers]
+
+    def run(events=None, cached=False):
+        for li, (q, k, v) in enumerate(layers):
             mark = None
             if events is not None:
                 def mark(i, stage):
                     ev = torch.cuda.Event(enable_timing=True)
                     ev.record(stream)
                     events.append((i, stage, ev))
-            sweep_layer(sw, q, k, v, o, mark)
+            sweep_layer(sw, q, k, v, o, mark, cache=caches[li] if cached else None)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} sweeps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    # per-stage breakdown from one extra evented sweep, enqueued behind a spin kernel so
-    # that host launch gaps do not count as stage time
-    events = []
-    hold_stream(400.0)
-    run(events)
-    torch.cuda.synchronize()
-    stage_us = {st: 0.0 for st in STAGES}
-    chunk_us = [0.0] * s.n_chunks
-    for (i, st, ev), (_, _, nxt) in zip(events, events[1:]):
-        if st == "end":
-            continue
-        dt = ev.elapsed_time(nxt) * 1e3
-        stage_us[st] += dt
-        chunk_us[i - 1] += dt
+    def timed(cached):
+        """(ms per sweep by wall clock, per-stage us, per-chunk us of one evented sweep)."""
+        tag = " (steady state)" if cached else ""
+        print(f"[bench] warmup {args.warmup}{tag}", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            run(cached=cached)
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} sweeps{tag}", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run(cached=cached)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # per-stage breakdown from one extra evented sweep, enqueued behind a spin kernel so
+        # that host launch gaps do not count as stage time
+        events = []
+        hold_stream(400.0)
+        run(events, cached=cached)
+        torch.cuda.synchronize()
+        stage_us = {st: 0.0 for st in STAGES}
+        chunk_us = [0.0] * s.n_chunks
+        for (i, st, ev), (_, _, nxt) in zip(events, events[1:]):
+            if st == "end":
+                continue
+            dt = ev.elapsed_time(nxt) * 1e3
+            stage_us[st] += dt
+            chunk_us[i - 1] += dt
+        return wall * 1e3 / args.steps, stage_us, chunk_us
+
+    ms_per_step, stage_us, chunk_us = timed(False)
+    ss_ms, ss_stage, ss_chunk = timed(True)
     t_attn = stage_us["attn"] * 1e-6
     attn_tflops = f_active / t_attn / 1e12
     cpu = None
@@ -380,6 +416,15 @@ def bench_sweep(args):
         "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
         "stage_us_per_sweep": {k: round(v, 1) for k, v in stage_us.items()},
         "chunk_us_per_sweep": [round(x, 1) for x in chunk_us],
+        "steady_state": {
+            "what": "per-layer pooled-key caches: each chunk pools its queries and only its own 3 key frames "
+                    "(chunk 1 its keys only) and selects over the cached prefix",
+            "value": f_dense / (ss_ms * 1e-3) / 1e12,
+            "ms_per_step": ss_ms,
+            "stage_us_per_sweep": {k: round(v, 1) for k, v in ss_stage.items()},
+            "chunk_us_per_sweep": [round(x, 1) for x in ss_chunk],
+            "pool_select_pct_of_attn": 100.0 * (sum(ss_stage.values()) - ss_stage["attn"]) / ss_stage["attn"],
+        },
         "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_of(s.name)},

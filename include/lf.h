@@ -27,11 +27,17 @@
  *     block j of frame f is f*n_bpf + j. Queries use the same rule on the chunk's own
  *     frames (query block r = frame r/n_bpf, block r%n_bpf).
  *   - Token tensors (x, q, k, v, o) are [B, H, tokens, d]: batch, head, token, channel,
- *     with each (b, h) slice contiguous. g.head_stride is the distance in tokens between
- *     consecutive (b, h) slices: 0 means packed (the tensor's own token count); a larger
- *     value addresses a prefix or a window of a bigger allocation, such as an
- *     autoregressive KV cache sized for the whole video (all token tensors of one call
- *     then share that stride). Pooled tensors and id lists are always packed.
+ *     with each (b, h) slice contiguous. Two strides give the distance in tokens between
+ *     consecutive (b, h) slices: g.head_stride for the query side (q, o, and lf_pool's
+ *     x) and g.kv_head_stride for the key side (k, v). 0 means packed (the tensor's own
+ *     token count); a larger value addresses a prefix or a window of a bigger
+ *     allocation, such as an autoregressive KV cache sized for the whole video.
+ *   - Pooled key tensors (k~ [B, H, frames*n_bpf, d], k^ [B, H, frames, d]) have their
+ *     (b, h) slices g.frame_stride frames apart: 0 means packed (the call's key-frame
+ *     count); a larger value addresses the first frames of a pooled-key cache sized for
+ *     the whole video, so the keys of each frame are pooled once when it enters the KV
+ *     cache and reused by every later chunk. Pooled queries and id lists are always
+ *     packed.
  */
 #ifndef LF_H
 #define LF_H
@@ -42,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LF_ABI_VERSION 2
+#define LF_ABI_VERSION 3
 
 typedef enum {
   LF_OK = 0,
@@ -55,10 +61,14 @@ typedef enum {
 typedef enum { LF_FP32 = 0, LF_BF16 = 1 } lf_dtype;
 
 /* B batch, H heads, d head dim, tokens_per_frame (tpf), block_size (bs), head_stride
- * (tokens between (b, h) slices of the token tensors; 0 = packed). */
+ * (tokens between (b, h) slices of q, o and lf_pool's x; 0 = packed), kv_head_stride
+ * (the same for k and v; 0 = packed), frame_stride (frames between (b, h) slices of the
+ * pooled key tensors; 0 = packed). */
 typedef struct {
   int32_t B, H, d, tokens_per_frame, block_size;
   int32_t head_stride;
+  int32_t kv_head_stride;
+  int32_t frame_stride;
 } lf_geom;
 
 /* Message for the last failing call on the calling thread ("" if none). The pointer
@@ -104,11 +114,14 @@ lf_status lf_block_budget(double s, int32_t n_kblocks, int32_t W_f, int32_t n_bp
  * lf_pool -- [S2] token compression by mean pooling.
  * x: [B, H, n_frames*tpf, d] in dtype dt (LF_BF16 or LF_FP32); with a nonzero
  *   g.head_stride the (b, h) slice starts at x + (b*H + h)*head_stride*d
- *   (head_stride >= n_frames*tpf).
+ *   (head_stride >= n_frames*tpf; g.kv_head_stride is not used).
  * blk_out: [B, H, n_frames*n_bpf, d] fp32, the mean of each block's tokens (q~ for the
  *   chunk's queries, k~ for keys), divided by the block's true token count.
  * frm_out: [B, H, n_frames, d] fp32, the mean of each frame's tpf tokens (k^), or NULL
- *   to skip (e.g. when pooling queries). Frame means are formed from the fp32 block
+ *   to skip (e.g. when pooling queries).
+ * Both outputs have their (b, h) slices g.frame_stride frames apart (0 = packed,
+ *   otherwise >= n_frames): pooling a chunk's new frames into a pooled-key cache passes
+ *   the cache at the first new frame. Frame means are formed from the fp32 block
  *   means weighted by their token counts.
  * Limits: d in {64, 128}; 1 <= bs <= tpf; tpf <= 65536; n_frames >= 1; B, H >= 1;
  *   head_stride = 0 or >= n_frames*tpf.
@@ -123,10 +136,11 @@ lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float
  * means only) and all keys (block and frame means), with results bitwise equal to
  * lf_pool(q, ..., n_qframes, q_blk, NULL) followed by lf_pool(k, ..., n_kframes, k_blk,
  * k_frm).
- * q: [B, H, n_qframes*tpf, d], k: [B, H, n_kframes*tpf, d], both in dtype dt; a nonzero
- *   g.head_stride applies to both (>= both token counts), 0 means each is packed.
- * q_blk: [B, H, n_qframes*n_bpf, d] fp32; k_blk: [B, H, n_kframes*n_bpf, d] fp32;
- *   k_frm: [B, H, n_kframes, d] fp32.
+ * q: [B, H, n_qframes*tpf, d], k: [B, H, n_kframes*tpf, d], both in dtype dt; their
+ *   (b, h) slices are g.head_stride (q) and g.kv_head_stride (k) tokens apart, each
+ *   0 (packed) or at least the tensor's token count.
+ * q_blk: [B, H, n_qframes*n_bpf, d] fp32 (packed); k_blk: [B, H, n_kframes*n_bpf, d] fp32;
+ *   k_frm: [B, H, n_kframes, d] fp32; the key outputs use g.frame_stride as lf_pool's do.
  * Limits and errors: those of lf_pool.
  * ------------------------------------------------------------------------------- */
 lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32_t n_qframes,
@@ -138,7 +152,8 @@ lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32
  * frames of M ranked by (score descending, frame id ascending) join the always-kept
  * frames (sink, recent and current-chunk frames, passed as `forced`) to form T_r.
  * q_blk: [B, H, n_qb, d] fp32 (lf_pool of the queries). k_frm: [B, H, n_kframes, d]
- *   fp32 (frame means of all key frames; only those in M are read).
+ *   fp32 (frame means of all key frames; only those in M are read), (b, h) slices
+ *   g.frame_stride frames apart (0 = packed).
  * mem, forced: HOST arrays of frame ids (n_mem, n_forced entries), each id in
  *   [0, n_kframes), no duplicates, the two sets disjoint; W_f (below) must be >= 1.
  * frames_out: [B, H, n_qb, W_f] int32, W_f = n_forced + min(k_f, n_mem), each row
@@ -157,7 +172,8 @@ lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, in
  * min(k_b, n_bpf) blocks J_r(tau) ranked by (score descending, j ascending). The mask
  * B_r(tau, j) = 1[tau in T_r, j in J_r(tau)] is emitted as an ascending list of global
  * block ids tau*n_bpf + j.
- * q_blk: [B, H, n_qb, d] fp32. k_blk: [B, H, n_kframes*n_bpf, d] fp32.
+ * q_blk: [B, H, n_qb, d] fp32. k_blk: [B, H, n_kframes*n_bpf, d] fp32, (b, h) slices
+ *   g.frame_stride frames apart (0 = packed).
  * frames: [B, H, n_qb, W_f] int32 device array, each row ascending and unique with ids
  *   in [0, n_kframes) (the output of lf_select_frames). A row breaking this gets
  *   unspecified list entries; nothing outside the buffers is read or written.
@@ -191,7 +207,9 @@ lf_status lf_select(const float* q_blk, const float* k_frm, const float* k_blk, 
  *   o_t = sum_u softmax_u(scale * <q_t, k_u>) v_u   (softmax over the listed tokens).
  * With every block listed this is dense attention (CAG's first chunk).
  * q, o: [B, H, n_qframes*tpf, d]; k, v: [B, H, n_kframes*tpf, d]; all in dtype dt.
- *   A nonzero g.head_stride (>= both token counts) applies to all four tensors.
+ *   The (b, h) slices of q and o are g.head_stride tokens apart, those of k and v
+ *   g.kv_head_stride tokens apart; each 0 (packed) or at least the token count (so a
+ *   chunk's packed queries can attend to a prefix of a KV cache sized for the video).
  * blocks: [B, H, n_qb, W_b] int32 device array, n_qb = n_qframes*n_bpf; ids should be
  *   unique (a repeated id is counted twice); ids outside [0, n_kframes*n_bpf) are
  *   skipped. A row with no valid id produces zeros.

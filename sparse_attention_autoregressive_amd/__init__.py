@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["Geom", "LfError", "lf_abi_version", "lf_cag_schedule", "lf_block_budget",
-           "lf_pool", "lf_select_frames", "lf_select_blocks", "lf_sparse_attn", "library_path",
+           "lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
+           "library_path",
            "n_bpf"]
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_INFEASIBLE, LF_ERR_HIP = range(5)
@@ -30,20 +31,33 @@ def library_path() -> str:
 
 
 class Geom(ctypes.Structure):
-    """lf_geom: batch, heads, head dim, tokens per frame, tokens per block, and the token
-    stride between (b, h) slices of the token tensors (0 = packed; the wrappers below fill
-    it in from the tensors they are given)."""
+    """lf_geom: batch, heads, head dim, tokens per frame, tokens per block, the token
+    strides between (b, h) slices of the query-side (q, o, lf_pool's x) and key-side (k, v)
+    token tensors, and the frame stride between (b, h) slices of the pooled key tensors
+    (0 = packed for each; the wrappers below fill them in from the tensors they are
+    given)."""
 
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("tokens_per_frame", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("head_stride", ctypes.c_int32)]
+                ("head_stride", ctypes.c_int32), ("kv_head_stride", ctypes.c_int32),
+                ("frame_stride", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"Geom(B={self.B}, H={self.H}, d={self.d}, tpf={self.tokens_per_frame}, "
-                f"bs={self.block_size}, head_stride={self.head_stride})")
+                f"bs={self.block_size}, head_stride={self.head_stride}, kv_head_stride={self.kv_head_stride}, "
+                f"frame_stride={self.frame_stride})")
 
-    def with_stride(self, head_stride: int) -> "Geom":
-        return Geom(self.B, self.H, self.d, self.tokens_per_frame, self.block_size, head_stride)
+    def _copy(self, **kw) -> "Geom":
+        f = {n: getattr(self, n) for n, _ in self._fields_}
+        f.update(kw)
+        return Geom(**f)
+
+    def with_stride(self, head_stride: int, kv_head_stride: Optional[int] = None) -> "Geom":
+        return self._copy(head_stride=head_stride,
+                          kv_head_stride=self.kv_head_stride if kv_head_stride is None else kv_head_stride)
+
+    def with_frame_stride(self, frame_stride: int) -> "Geom":
+        return self._copy(frame_stride=frame_stride)
 
 
 def n_bpf(g: Geom) -> int:
@@ -123,10 +137,36 @@ def _tokens(t: torch.Tensor, name: str, g: Geom, n_tokens: int) -> int:
     return sh // g.d
 
 
-def _common_stride(g: Geom, strides: Sequence[int]) -> Geom:
+def _pooled(t: torch.Tensor, name: str, g: Geom, n_frames: int, per_frame: int) -> int:
+    """Checks a pooled key tensor [B, H, n_frames*per_frame, d] fp32 (per_frame = blocks per
+    frame for block means, 1 for frame means) whose (b, h) slices are contiguous and evenly
+    spaced (packed, or the first frames of a cache sized for more); returns its frame
+    stride."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if tuple(t.shape) != (g.B, g.H, n_frames * per_frame, g.d):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(g.B, g.H, n_frames * per_frame, g.d)}")
+    sb, sh, sr, sc = t.stride()
+    unit = per_frame * g.d
+    if sc != 1 or sr != g.d or sh % unit != 0 or (g.B > 1 and sb != g.H * sh):
+        raise ValueError(f"{name}: each (b, h) slice must be contiguous and the slices evenly spaced")
+    return sh // unit
+
+
+def _frame_geom(g: Geom, n_frames: int, strides: Sequence[int]) -> Geom:
+    """g with the frame stride of the pooled key tensors of one call (0 when packed)."""
     if len(set(strides)) != 1:
-        raise ValueError(f"token tensors of one call must share their head stride, got {strides}")
-    return g.with_stride(strides[0])
+        raise ValueError(f"pooled key tensors of one call must share their frame stride, got {strides}")
+    return g.with_frame_stride(0 if strides[0] == n_frames else strides[0])
+
+
+def _shared(names: str, strides: Sequence[int], n_tokens: int) -> int:
+    """The head stride that tensors `names` share (0 when packed)."""
+    if len(set(strides)) != 1:
+        raise ValueError(f"{names} must share their head stride, got {strides}")
+    return 0 if strides[0] == n_tokens else strides[0]
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -174,15 +214,20 @@ def lf_pool(x: torch.Tensor, g: Geom, n_frames: int, blk_out: Optional[torch.Ten
     if frm_out is None and with_frames:
         frm_out = torch.empty((g.B, g.H, n_frames, g.d), dtype=torch.float32, device=x.device)
     gx = g.with_stride(_tokens(x, "x", g, n_frames * g.tokens_per_frame))
-    _check(lib.lf_pool(x.data_ptr(), _dtype_code(x), gx, n_frames, _dev(blk_out, "blk_out"),
-                       None if frm_out is None else _dev(frm_out, "frm_out"), _stream(x)))
+    fs = [_pooled(blk_out, "blk_out", g, n_frames, nb)]
+    if frm_out is not None:
+        fs.append(_pooled(frm_out, "frm_out", g, n_frames, 1))
+    gx = _frame_geom(gx, n_frames, fs)
+    _check(lib.lf_pool(x.data_ptr(), _dtype_code(x), gx, n_frames, blk_out.data_ptr(),
+                       None if frm_out is None else frm_out.data_ptr(), _stream(x)))
     return blk_out, frm_out
 
 
 def lf_pool_qk(q: torch.Tensor, k: torch.Tensor, g: Geom, n_qframes: int, n_kframes: int,
                q_blk: Optional[torch.Tensor] = None, k_blk: Optional[torch.Tensor] = None,
                k_frm: Optional[torch.Tensor] = None):
-    """Query block means and key block + frame means in one launch: (q_blk, k_blk, k_frm)."""
+    """Query block means and key block + frame means in one launch: (q_blk, k_blk, k_frm).
+    q_blk is packed; k_blk and k_frm may be the first n_kframes frames of bigger caches."""
     lib = _load()
     nb = n_bpf(g)
     f32, dev = torch.float32, q.device
@@ -195,10 +240,10 @@ def lf_pool_qk(q: torch.Tensor, k: torch.Tensor, g: Geom, n_qframes: int, n_kfra
     if q.dtype != k.dtype:
         raise TypeError("q and k must share a dtype")
     lq, lk = n_qframes * g.tokens_per_frame, n_kframes * g.tokens_per_frame
-    strides = [_tokens(q, "q", g, lq), _tokens(k, "k", g, lk)]
-    gg = g.with_stride(0) if strides == [lq, lk] else _common_stride(g, strides)
+    gg = g.with_stride(_shared("q", [_tokens(q, "q", g, lq)], lq), _shared("k", [_tokens(k, "k", g, lk)], lk))
+    gg = _frame_geom(gg, n_kframes, [_pooled(k_blk, "k_blk", g, n_kframes, nb), _pooled(k_frm, "k_frm", g, n_kframes, 1)])
     _check(lib.lf_pool_qk(q.data_ptr(), k.data_ptr(), _dtype_code(q), gg, n_qframes, n_kframes,
-                          _dev(q_blk, "q_blk"), _dev(k_blk, "k_blk"), _dev(k_frm, "k_frm"), _stream(q)))
+                          _dev(q_blk, "q_blk"), k_blk.data_ptr(), k_frm.data_ptr(), _stream(q)))
     return q_blk, k_blk, k_frm
 
 
@@ -210,7 +255,8 @@ def lf_select_frames(q_blk: torch.Tensor, k_frm: torch.Tensor, g: Geom, n_qb: in
     W_f = len(forced) + min(k_f, len(mem))
     if out is None:
         out = torch.empty((g.B, g.H, n_qb, max(W_f, 1)), dtype=torch.int32, device=q_blk.device)
-    _check(lib.lf_select_frames(_dev(q_blk, "q_blk"), _dev(k_frm, "k_frm"), g, n_qb, n_kframes,
+    g = _frame_geom(g, n_kframes, [_pooled(k_frm, "k_frm", g, n_kframes, 1)])
+    _check(lib.lf_select_frames(_dev(q_blk, "q_blk"), k_frm.data_ptr(), g, n_qb, n_kframes,
                                 _i32_array(mem), len(mem), _i32_array(forced), len(forced), k_f,
                                 _dev(out, "out"), _stream(q_blk)))
     return out
@@ -224,7 +270,8 @@ def lf_select_blocks(q_blk: torch.Tensor, k_blk: torch.Tensor, g: Geom, n_qb: in
     W_b = W_f * min(k_b, n_bpf(g))
     if out is None:
         out = torch.empty((g.B, g.H, n_qb, W_b), dtype=torch.int32, device=q_blk.device)
-    _check(lib.lf_select_blocks(_dev(q_blk, "q_blk"), _dev(k_blk, "k_blk"), g, n_qb, n_kframes,
+    g = _frame_geom(g, n_kframes, [_pooled(k_blk, "k_blk", g, n_kframes, n_bpf(g))])
+    _check(lib.lf_select_blocks(_dev(q_blk, "q_blk"), k_blk.data_ptr(), g, n_qb, n_kframes,
                                 _dev(frames, "frames"), W_f, k_b, _dev(out, "out"), _stream(q_blk)))
     return out
 
@@ -242,7 +289,9 @@ def lf_select(q_blk: torch.Tensor, k_frm: torch.Tensor, k_blk: torch.Tensor, g: 
         frames_out = torch.empty((g.B, g.H, n_qb, max(W_f, 1)), dtype=torch.int32, device=dev)
     if blocks_out is None:
         blocks_out = torch.empty((g.B, g.H, n_qb, W_b), dtype=torch.int32, device=dev)
-    _check(lib.lf_select(_dev(q_blk, "q_blk"), _dev(k_frm, "k_frm"), _dev(k_blk, "k_blk"), g, n_qb, n_kframes,
+    g = _frame_geom(g, n_kframes, [_pooled(k_frm, "k_frm", g, n_kframes, 1),
+                                   _pooled(k_blk, "k_blk", g, n_kframes, n_bpf(g))])
+    _check(lib.lf_select(_dev(q_blk, "q_blk"), k_frm.data_ptr(), k_blk.data_ptr(), g, n_qb, n_kframes,
                          _i32_array(mem), len(mem), _i32_array(forced), len(forced), k_f, k_b,
                          None if frames_out is None else _dev(frames_out, "frames_out"),
                          _dev(blocks_out, "blocks_out"), _stream(q_blk)))
@@ -259,8 +308,8 @@ def lf_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geom, n
     if not (q.dtype == k.dtype == v.dtype == out.dtype):
         raise TypeError("q, k, v and out must share a dtype")
     lq, lk = n_qframes * g.tokens_per_frame, n_kframes * g.tokens_per_frame
-    strides = [_tokens(q, "q", g, lq), _tokens(k, "k", g, lk), _tokens(v, "v", g, lk), _tokens(out, "out", g, lq)]
-    ga = g.with_stride(0) if strides == [lq, lk, lk, lq] else _common_stride(g, strides)
+    ga = g.with_stride(_shared("q and out", [_tokens(q, "q", g, lq), _tokens(out, "out", g, lq)], lq),
+                       _shared("k and v", [_tokens(k, "k", g, lk), _tokens(v, "v", g, lk)], lk))
     _check(lib.lf_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               _dtype_code(q), ga, n_qframes, n_kframes, _dev(blocks, "blocks"),
                               blocks.shape[-1], float(scale), _stream(q)))

@@ -36,12 +36,23 @@ lf_status check_geom(const lf_geom& g, const char* fn) {
   if (g.block_size < 1 || g.block_size > g.tokens_per_frame)
     return fail(LF_ERR_INVALID_ARG, "%s: block_size must be in [1, tokens_per_frame]", fn);
   if (g.d < 1) return fail(LF_ERR_INVALID_ARG, "%s: d must be >= 1", fn);
-  if (g.head_stride < 0) return fail(LF_ERR_INVALID_ARG, "%s: head_stride must be >= 0", fn);
+  if (g.head_stride < 0 || g.kv_head_stride < 0)
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride and kv_head_stride must be >= 0", fn);
+  if (g.frame_stride < 0) return fail(LF_ERR_INVALID_ARG, "%s: frame_stride must be >= 0", fn);
   if (g.d != 64 && g.d != 128) return fail(LF_ERR_UNSUPPORTED, "%s: d=%d unsupported (64 or 128)", fn, g.d);
   return LF_OK;
 }
 
 bool fits_int(long long v) { return v >= 0 && v <= 0x7fffffffLL; }
+
+// Frames between (b, h) slices of the pooled key tensors: g.frame_stride, or the call's
+// key-frame count when it is 0. Fails when a nonzero stride is below that count.
+lf_status pooled_stride(const lf_geom& g, int32_t n_kframes, int* out, const char* fn) {
+  if (g.frame_stride != 0 && g.frame_stride < n_kframes)
+    return fail(LF_ERR_INVALID_ARG, "%s: frame_stride %d < key-frame count %d", fn, g.frame_stride, n_kframes);
+  *out = g.frame_stride ? g.frame_stride : n_kframes;
+  return LF_OK;
+}
 
 // Clears an error left by earlier, unrelated HIP work so it is not reported as ours.
 void pending_error() { (void)hipGetLastError(); }
@@ -82,6 +93,9 @@ lf_status check_frame_stage(const float* q_blk, const float* k_frm, lf_geom g, i
     seen[f] = true;
     a.lists.forced[i] = static_cast<int16_t>(f);
   }
+  if (lf_status st = pooled_stride(g, n_kframes, &a.kf_stride, fn)) return st;
+  if (!fits_int(static_cast<long long>(g.B) * g.H * a.kf_stride * g.d))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   a.k_eff = k_f < n_mem ? k_f : n_mem;
   a.W_f = n_forced + a.k_eff;
   if (a.W_f < 1) return fail(LF_ERR_INVALID_ARG, "%s: empty frame set (W_f = 0)", fn);
@@ -107,8 +121,10 @@ lf_status check_block_stage(const float* k_blk, lf_geom g, int32_t n_qb, int32_t
   if (!k_blk || !blocks_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!aligned16(k_blk) || (reinterpret_cast<uintptr_t>(blocks_out) & 3u))
     return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  if (lf_status st = pooled_stride(g, n_kframes, &a.kf_stride, fn)) return st;
   a.kb_eff = k_b < n_bpf ? k_b : n_bpf;
-  if (!fits_int(static_cast<long long>(g.B) * g.H * n_qb) || !fits_int(static_cast<long long>(W_f) * a.kb_eff))
+  if (!fits_int(static_cast<long long>(g.B) * g.H * n_qb) || !fits_int(static_cast<long long>(W_f) * a.kb_eff) ||
+      !fits_int(static_cast<long long>(g.B) * g.H * a.kf_stride * n_bpf))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   a.k_blk = k_blk;
   a.blocks_out = blocks_out;
@@ -200,9 +216,12 @@ lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float
   if (g.head_stride != 0 && g.head_stride < len)
     return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < n_frames*tpf = %lld", fn, g.head_stride, len);
   const long long stride = g.head_stride ? g.head_stride : len;
+  int out_stride = 0;
+  if (lf_status st = pooled_stride(g, n_frames, &out_stride, fn)) return st;
+  if (!fits_int(BH * out_stride * n_bpf)) return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   pending_error();
   return hip_status(lf::launch_pool(x, dt == LF_BF16, g.d, static_cast<int>(BH), n_frames,
-                                    g.tokens_per_frame, g.block_size, n_bpf, stride, blk_out, frm_out,
+                                    g.tokens_per_frame, g.block_size, n_bpf, stride, out_stride, blk_out, frm_out,
                                     static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -223,13 +242,17 @@ lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32
   if (!fits_int(BH * n_kframes * n_bpf) || !fits_int(BH * n_qframes * n_bpf + BH * n_kframes) ||
       !fits_int(lq) || !fits_int(lk))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
-  if (g.head_stride != 0 && (g.head_stride < lq || g.head_stride < lk))
-    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d is below the query or key token count", fn,
-                g.head_stride);
+  if (g.head_stride != 0 && g.head_stride < lq)
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < query token count %lld", fn, g.head_stride, lq);
+  if (g.kv_head_stride != 0 && g.kv_head_stride < lk)
+    return fail(LF_ERR_INVALID_ARG, "%s: kv_head_stride %d < key token count %lld", fn, g.kv_head_stride, lk);
+  int k_out_stride = 0;
+  if (lf_status st = pooled_stride(g, n_kframes, &k_out_stride, fn)) return st;
+  if (!fits_int(BH * k_out_stride * n_bpf)) return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   pending_error();
   return hip_status(lf::launch_pool_qk(q, k, dt == LF_BF16, g.d, static_cast<int>(BH), n_qframes, n_kframes,
                                        g.tokens_per_frame, g.block_size, n_bpf, g.head_stride ? g.head_stride : lq,
-                                       g.head_stride ? g.head_stride : lk, q_blk, k_blk, k_frm,
+                                       g.kv_head_stride ? g.kv_head_stride : lk, k_out_stride, q_blk, k_blk, k_frm,
                                        static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -308,16 +331,17 @@ lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, l
   // the bf16 kernel addresses one (b, h) slice of K and V with 32-bit byte offsets
   if (!fits_int(BH * n_qb) || !fits_int(n_kb) || !fits_int(lq) || !fits_int(lk * g.d * 4))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
-  if (g.head_stride != 0 && (g.head_stride < lq || g.head_stride < lk))
-    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d is below the query or key token count", fn,
-                g.head_stride);
+  if (g.head_stride != 0 && g.head_stride < lq)
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < query token count %lld", fn, g.head_stride, lq);
+  if (g.kv_head_stride != 0 && g.kv_head_stride < lk)
+    return fail(LF_ERR_INVALID_ARG, "%s: kv_head_stride %d < key token count %lld", fn, g.kv_head_stride, lk);
   lf::AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.blocks = blocks;
   a.BH = static_cast<int>(BH); a.n_qb = static_cast<int>(n_qb); a.n_kb = static_cast<int>(n_kb);
   a.W_b = W_b; a.tpf = g.tokens_per_frame; a.bs = g.block_size; a.n_bpf = n_bpf;
   a.lq = static_cast<int>(lq); a.lk = static_cast<int>(lk);
   a.q_stride = g.head_stride ? g.head_stride : lq;
-  a.kv_stride = g.head_stride ? g.head_stride : lk;
+  a.kv_stride = g.kv_head_stride ? g.kv_head_stride : lk;
   a.scale_log2 = scale * 1.4426950408889634f;
   pending_error();
   const hipStream_t st = static_cast<hipStream_t>(stream);

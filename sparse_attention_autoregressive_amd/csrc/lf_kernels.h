@@ -14,15 +14,17 @@ struct FrameLists {
   int16_t forced[kMaxFrames];
 };
 
-// x_stride: tokens between consecutive (b, h) slices of x.
+// x_stride: tokens between consecutive (b, h) slices of x; out_stride: frames between
+// consecutive (b, h) slices of the outputs.
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
-                       int n_bpf, long long x_stride, float* blk, float* frm, hipStream_t st);
+                       int n_bpf, long long x_stride, int out_stride, float* blk, float* frm, hipStream_t st);
 
 // Queries (block means) and keys (block and frame means) in one launch; q_stride and
-// k_stride: tokens between consecutive (b, h) slices of q and k.
+// k_stride: tokens between consecutive (b, h) slices of q and k; k_out_stride: frames
+// between (b, h) slices of the pooled keys (q_blk is packed).
 hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH, int n_qframes, int n_kframes,
-                          int tpf, int bs, int n_bpf, long long q_stride, long long k_stride, float* q_blk,
-                          float* k_blk, float* k_frm, hipStream_t st);
+                          int tpf, int bs, int n_bpf, long long q_stride, long long k_stride, int k_out_stride,
+                          float* q_blk, float* k_blk, float* k_frm, hipStream_t st);
 
 // One launch of the selection kernel over n_rows = B*H*n_qb rows. Frame stage: reads
 // q_blk, k_frm, lists, n_mem, n_forced, k_eff and writes frames_out (if set). Block
@@ -36,6 +38,7 @@ struct SelectArgs {
   int* frames_out;
   int* blocks_out;
   int n_qb, n_kframes, n_bpf;
+  int kf_stride;        // frames between (b, h) slices of k_frm and k_blk
   int n_mem, n_forced, k_eff, W_f, kb_eff;
   FrameLists lists;
 };

@@ -95,8 +95,8 @@ __device__ __forceinline__ void block_sum(const T* __restrict__ frame, int j, in
 // block means only.
 template <typename T, int D, bool FRAMES, int W>
 __device__ __forceinline__ void pool_part(const T* __restrict__ x, float* __restrict__ blk, float* __restrict__ frm,
-                                          int n_frames, int tpf, int bs, int n_bpf, long long x_stride, int wg,
-                                          float (*fs)[D]) {
+                                          int n_frames, int tpf, int bs, int n_bpf, long long x_stride,
+                                          int out_stride, int wg, float (*fs)[D]) {
   constexpr int E = Chunk16<T>::E;
   constexpr int C = D / E;
   const int groups = FRAMES ? 1 : (n_bpf + W - 1) / W;
@@ -105,7 +105,8 @@ __device__ __forceinline__ void pool_part(const T* __restrict__ x, float* __rest
   const int bh = bf / n_frames, f = bf - bh * n_frames;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const T* frame = x + (static_cast<size_t>(bh) * x_stride + static_cast<size_t>(f) * tpf) * D;
-  float* blk_row = blk + static_cast<size_t>(bf) * n_bpf * D;
+  const size_t of = static_cast<size_t>(bh) * out_stride + f;   // output frame slot
+  float* blk_row = blk + of * n_bpf * D;
 
   float fsum[E];
 #pragma unroll
@@ -137,17 +138,17 @@ __device__ __forceinline__ void pool_part(const T* __restrict__ x, float* __rest
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) t += fs[w][threadIdx.x];
-    frm[static_cast<size_t>(bf) * D + threadIdx.x] = t / static_cast<float>(tpf);
+    frm[of * D + threadIdx.x] = t / static_cast<float>(tpf);
   }
 }
 
 template <typename T, int D, bool FRAMES>
 __global__ void __launch_bounds__((FRAMES ? kFrameWaves : kPoolWaves) * kWave) pool_kernel(
     const T* __restrict__ x, float* __restrict__ blk, float* __restrict__ frm, int n_frames, int tpf, int bs,
-    int n_bpf, long long x_stride) {
+    int n_bpf, long long x_stride, int out_stride) {
   constexpr int W = FRAMES ? kFrameWaves : kPoolWaves;
   __shared__ __attribute__((aligned(16))) float fs[W][D];
-  pool_part<T, D, FRAMES, W>(x, blk, frm, n_frames, tpf, bs, n_bpf, x_stride, blockIdx.x, fs);
+  pool_part<T, D, FRAMES, W>(x, blk, frm, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blockIdx.x, fs);
 }
 
 // Queries (block means) and keys (block and frame means) in one launch: the first n_qwg
@@ -156,65 +157,66 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kFrameWaves * kWave) pool_qk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ q_blk, float* __restrict__ k_blk,
     float* __restrict__ k_frm, int n_qframes, int n_kframes, int tpf, int bs, int n_bpf, long long q_stride,
-    long long k_stride, int n_qwg) {
+    long long k_stride, int k_out_stride, int n_qwg) {
   __shared__ __attribute__((aligned(16))) float fs[kFrameWaves][D];
   const int wg = blockIdx.x;
   if (wg < n_qwg)
-    pool_part<T, D, false, kFrameWaves>(q, q_blk, nullptr, n_qframes, tpf, bs, n_bpf, q_stride, wg, fs);
+    pool_part<T, D, false, kFrameWaves>(q, q_blk, nullptr, n_qframes, tpf, bs, n_bpf, q_stride, n_qframes, wg, fs);
   else
-    pool_part<T, D, true, kFrameWaves>(k, k_blk, k_frm, n_kframes, tpf, bs, n_bpf, k_stride, wg - n_qwg, fs);
+    pool_part<T, D, true, kFrameWaves>(k, k_blk, k_frm, n_kframes, tpf, bs, n_bpf, k_stride, k_out_stride,
+                                       wg - n_qwg, fs);
 }
 
 template <typename T, int D>
 static hipError_t launch_pool_t(const void* x, int BH, int n_frames, int tpf, int bs, int n_bpf,
-                                long long x_stride, float* blk, float* frm, hipStream_t st) {
+                                long long x_stride, int out_stride, float* blk, float* frm, hipStream_t st) {
   const unsigned frames = static_cast<unsigned>(BH) * n_frames;
   if (frm != nullptr) {
     hipLaunchKernelGGL((pool_kernel<T, D, true>), dim3(frames), dim3(kFrameWaves * kWave), 0, st,
-                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride);
+                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride, out_stride);
   } else {
     const unsigned groups = (n_bpf + kPoolWaves - 1) / kPoolWaves;
     hipLaunchKernelGGL((pool_kernel<T, D, false>), dim3(frames * groups), dim3(kPoolWaves * kWave), 0, st,
-                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride);
+                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride, out_stride);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t launch_pool_qk_t(const void* q, const void* k, int BH, int n_qframes, int n_kframes, int tpf,
-                                   int bs, int n_bpf, long long q_stride, long long k_stride, float* q_blk,
-                                   float* k_blk, float* k_frm, hipStream_t st) {
+                                   int bs, int n_bpf, long long q_stride, long long k_stride, int k_out_stride,
+                                   float* q_blk, float* k_blk, float* k_frm, hipStream_t st) {
   const int n_qwg = BH * n_qframes * ((n_bpf + kFrameWaves - 1) / kFrameWaves);
   const unsigned grid = static_cast<unsigned>(n_qwg) + static_cast<unsigned>(BH) * n_kframes;
   hipLaunchKernelGGL((pool_qk_kernel<T, D>), dim3(grid), dim3(kFrameWaves * kWave), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), q_blk, k_blk, k_frm, n_qframes, n_kframes,
-                     tpf, bs, n_bpf, q_stride, k_stride, n_qwg);
+                     tpf, bs, n_bpf, q_stride, k_stride, k_out_stride, n_qwg);
   return hipGetLastError();
 }
 
 hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH, int n_qframes, int n_kframes,
-                          int tpf, int bs, int n_bpf, long long q_stride, long long k_stride, float* q_blk,
-                          float* k_blk, float* k_frm, hipStream_t st) {
+                          int tpf, int bs, int n_bpf, long long q_stride, long long k_stride, int k_out_stride,
+                          float* q_blk, float* k_blk, float* k_frm, hipStream_t st) {
   if (bf16) {
     return d == 128 ? launch_pool_qk_t<__bf16, 128>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
-                                                    k_stride, q_blk, k_blk, k_frm, st)
+                                                    k_stride, k_out_stride, q_blk, k_blk, k_frm, st)
                     : launch_pool_qk_t<__bf16, 64>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
-                                                   k_stride, q_blk, k_blk, k_frm, st);
+                                                   k_stride, k_out_stride, q_blk, k_blk, k_frm, st);
   }
   return d == 128 ? launch_pool_qk_t<float, 128>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
-                                                 k_stride, q_blk, k_blk, k_frm, st)
+                                                 k_stride, k_out_stride, q_blk, k_blk, k_frm, st)
                   : launch_pool_qk_t<float, 64>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride, k_stride,
-                                                q_blk, k_blk, k_frm, st);
+                                                k_out_stride, q_blk, k_blk, k_frm, st);
 }
 
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
-                       int n_bpf, long long x_stride, float* blk, float* frm, hipStream_t st) {
+                       int n_bpf, long long x_stride, int out_stride, float* blk, float* frm, hipStream_t st) {
   if (bf16) {
-    return d == 128 ? launch_pool_t<__bf16, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st)
-                    : launch_pool_t<__bf16, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st);
+    return d == 128 ? launch_pool_t<__bf16, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st)
+                    : launch_pool_t<__bf16, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st);
   }
-  return d == 128 ? launch_pool_t<float, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st)
-                  : launch_pool_t<float, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, blk, frm, st);
+  return d == 128 ? launch_pool_t<float, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st)
+                  : launch_pool_t<float, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st);
 }
 
 }  // namespace lf

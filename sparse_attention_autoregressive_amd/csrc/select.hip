@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
 
   int W_f = a.W_f;
   if (FRAMES) {
-    const float* kf = a.k_frm + static_cast<size_t>(bh) * a.n_kframes * D;
+    const float* kf = a.k_frm + static_cast<size_t>(bh) * a.kf_stride * D;
     for (int e = grp; e < a.n_mem; e += kGroups) {
       const int f = a.lists.mem[e];
       const float s = group_dot<D>(q, kf + static_cast<size_t>(f) * D, c);
@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
     }
     return;
   }
-  const float* kbase = a.k_blk + static_cast<size_t>(bh) * a.n_kframes * n_bpf * D;
+  const float* kbase = a.k_blk + static_cast<size_t>(bh) * a.kf_stride * n_bpf * D;
   for (int t0 = 0; t0 < W_f; t0 += kSlots) {
     const int nt = min(kSlots, W_f - t0);
     for (int e = grp; e < nt * n_bpf; e += kGroups) {

@@ -3,8 +3,15 @@
 Order (Light Forcing summary, execution flow, stages 2-3): pool the chunk's queries
 (block means q~), pool all keys (block means k~ and frame means k^), frame top-k per
 query block (T_r) and block top-k inside the chosen frames (the mask B_r as id lists)
-in one selection launch, block-sparse attention. The two poolings share one launch. All outputs are allocated once in a `Workspace`, so repeated
-calls (timing loops, the per-layer sweep) allocate nothing.
+in one selection launch, block-sparse attention. The two poolings share one launch.
+All outputs are allocated once in a `Workspace`, so repeated calls (timing loops, the
+per-layer sweep) allocate nothing.
+
+Steady state (`PooledKeyCache`): a frame's keys do not change once the frame is in the
+KV cache, so their block and frame means are computed once and kept; each later call
+pools only the chunk's queries and its own key frames, and selection reads the cached
+prefix. Results are bitwise those of the uncached path, since every frame's means are
+computed by the same code from the same tokens.
 """
 from __future__ import annotations
 
@@ -113,6 +120,66 @@ def hsa_chunk(ws: Workspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     return ws.o if out is None else out
 
 
+class PooledKeyCache:
+    """Pooled keys of one layer for every frame of a clip: block means k~
+    [B, H, n_frames*n_bpf, d] and frame means k^ [B, H, n_frames, d], fp32. Selection over
+    the key prefix k_{:i} (Light Forcing summary, stage 3) reads the first frames; a
+    frame's entries are written when its keys are pooled."""
+
+    def __init__(self, g: Geom, n_frames: int, device):
+        self.geom, self.n_frames, self.nb = g, n_frames, n_bpf(g)
+        f32 = torch.float32
+        self.k_blk = torch.empty((g.B, g.H, n_frames * self.nb, g.d), dtype=f32, device=device)
+        self.k_frm = torch.empty((g.B, g.H, n_frames, g.d), dtype=f32, device=device)
+
+    def blk(self, f0: int, f1: int) -> torch.Tensor:
+        """Block means of frames [f0, f1) (a view)."""
+        return self.k_blk[:, :, f0 * self.nb:f1 * self.nb]
+
+    def frm(self, f0: int, f1: int) -> torch.Tensor:
+        """Frame means of frames [f0, f1) (a view)."""
+        return self.k_frm[:, :, f0:f1]
+
+
+def new_frames(p: ChunkPlan) -> int:
+    """First key frame of the chunk itself: its keys are the last n_qframes of the prefix."""
+    return p.n_kframes - p.n_qframes
+
+
+def pool_cached(ws: Workspace, cache: PooledKeyCache, q: torch.Tensor, k: torch.Tensor):
+    """Pools the chunk's queries and only its own key frames (the last n_qframes of the
+    key prefix k) into `cache`, in one launch."""
+    p = ws.plan
+    f0, tpf = new_frames(p), p.geom.tokens_per_frame
+    lf_pool_qk(q, k[:, :, f0 * tpf:], p.geom, p.n_qframes, p.n_qframes, ws.q_blk,
+               cache.blk(f0, p.n_kframes), cache.frm(f0, p.n_kframes))
+
+
+def pool_keys_cached(p: ChunkPlan, cache: PooledKeyCache, k: torch.Tensor):
+    """Pools only the chunk's own key frames into `cache` (a dense chunk needs no pooled
+    queries, but later chunks select over its keys)."""
+    f0, tpf = new_frames(p), p.geom.tokens_per_frame
+    lf_pool(k[:, :, f0 * tpf:], p.geom, p.n_qframes, blk_out=cache.blk(f0, p.n_kframes),
+            frm_out=cache.frm(f0, p.n_kframes))
+
+
+def select_cached(ws: Workspace, cache: PooledKeyCache):
+    """Both selection stages over the cached pooled keys of the key prefix."""
+    p = ws.plan
+    lf_select(ws.q_blk, cache.frm(0, p.n_kframes), cache.blk(0, p.n_kframes), p.geom, p.n_qb, p.n_kframes,
+              p.mem, p.forced, p.k_f, p.k_b, frames_out=ws.frames, blocks_out=ws.blocks)
+
+
+def hsa_chunk_cached(ws: Workspace, cache: PooledKeyCache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     out=None) -> torch.Tensor:
+    """hsa_chunk in steady state: the pooled keys of the earlier frames come from `cache`
+    (filled by earlier chunks); the chunk's own key frames are pooled into it."""
+    pool_cached(ws, cache, q, k)
+    select_cached(ws, cache)
+    attend(ws, q, k, v, out)
+    return ws.o if out is None else out
+
+
 # ------------------------------------------------------------------ Chunk-Aware Growth sweep
 @dataclass
 class SweepPlan:
@@ -175,12 +242,14 @@ class SweepWorkspace:
 
 
 def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                o: torch.Tensor, mark=None) -> torch.Tensor:
+                o: torch.Tensor, mark=None, cache: PooledKeyCache = None) -> torch.Tensor:
     """All chunks of one layer in order. q, k, v, o: [B, H, n_frames*tpf, d] holding the
     whole clip; chunk i reads its query frames and the key prefix as views and writes its
     frames of o. Enqueued on the current stream; returns o. `mark(i, stage)`, if given,
     is called before each stage ("pool", "select", "attn") and with stage
-    "end" after chunk i (e.g. to record timing events)."""
+    "end" after chunk i (e.g. to record timing events). With a `cache` (this layer's,
+    sized for the clip), every chunk pools only its own key frames into it, the dense
+    first chunk included, and selection reads the cached prefix: the same outputs."""
     sp = sw.plan
     tpf = sp.geom.tokens_per_frame
     tick = mark if mark is not None else (lambda i, stage: None)
@@ -188,13 +257,22 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
         a, b = (i - 1) * sp.frames_per_chunk * tpf, i * sp.frames_per_chunk * tpf
         qv, ov, kv, vv = q[:, :, a:b], o[:, :, a:b], k[:, :, :b], v[:, :, :b]
         if sp.dense(i):
+            if cache is not None:
+                tick(i, "pool")
+                pool_keys_cached(p, cache, kv)
             tick(i, "attn")
             lf_sparse_attn(qv, kv, vv, p.geom, p.n_qframes, p.n_kframes, sw.full[i], p.scale, out=ov)
         else:
             tick(i, "pool")
-            pool(ws, qv, kv)
+            if cache is None:
+                pool(ws, qv, kv)
+            else:
+                pool_cached(ws, cache, qv, kv)
             tick(i, "select")
-            select(ws)
+            if cache is None:
+                select(ws)
+            else:
+                select_cached(ws, cache)
             tick(i, "attn")
             attend(ws, qv, kv, vv, ov)
         tick(i, "end")

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
             "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lf.lf_abi_version() == 2
+    assert lf.lf_abi_version() == 3
 
 
 @pytest.mark.parametrize("n,T,s_base,s_t", [(7, 4, 0.95, 0.8), (7, 4, 0.95, 0.85), (5, 2, 0.9, 0.6),
@@ -184,7 +184,12 @@ def test_pool_qk_validation():
     _err(c.lf_pool_qk(F, None, 1, g, 3, 21, F, F, F, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_pool_qk(F, F, 1, g, 3, 21, F, F, F + 4, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_pool_qk(F, F, 7, g, 3, 21, F, F, F, None), lf.LF_ERR_UNSUPPORTED)
-    _err(c.lf_pool_qk(F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 4680), 3, 21, F, F, F, None), lf.LF_ERR_INVALID_ARG)
+    # query stride below the 3-frame query range, key stride below the 21-frame key range
+    _err(c.lf_pool_qk(F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 4679), 3, 21, F, F, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool_qk(F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, 21 * 1560 - 1), 3, 21, F, F, F, None),
+         lf.LF_ERR_INVALID_ARG)
+    # pooled-key outputs: frame stride below the 21 pooled frames
+    _err(c.lf_pool_qk(F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, 0, 20), 3, 21, F, F, F, None), lf.LF_ERR_INVALID_ARG)
 
 
 def test_head_stride_validation():
@@ -193,11 +198,33 @@ def test_head_stride_validation():
     # pooling 3 frames of 1560 tokens needs a head stride of 0 or >= 4680
     _err(c.lf_pool(F, 1, lf.Geom(1, 2, 128, 1560, 64, 4679), 3, F, None, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_pool(F, 1, lf.Geom(1, 2, 128, 1560, 64, -1), 3, F, None, None), lf.LF_ERR_INVALID_ARG)
-    # attention: the stride covers both the query (3 frames) and key (21 frames) ranges
-    _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 21 * 1560 - 1), 3, 21, F, 64, 0.1, None),
+    # attention: the query stride covers the 3 query frames, the key stride the 21 key frames
+    _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 3 * 1560 - 1), 3, 21, F, 64, 0.1, None),
+         lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, 21 * 1560 - 1), 3, 21, F, 64, 0.1,
+                          None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_sparse_attn(F, F, F, F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, -5), 3, 21, F, 64, 0.1, None),
          lf.LF_ERR_INVALID_ARG)
     g = lf.Geom(1, 2, 128, 1560, 64)
-    assert g.head_stride == 0 and g.with_stride(7).head_stride == 7
+    assert g.head_stride == 0 and g.kv_head_stride == 0 and g.frame_stride == 0
+    g2 = g.with_stride(7, 9).with_frame_stride(21)
+    assert (g2.head_stride, g2.kv_head_stride, g2.frame_stride) == (7, 9, 21)
+    assert g2.with_stride(8).kv_head_stride == 9
+
+
+def test_frame_stride_validation():
+    c = _c()
+    F = FAKE
+    arr = lf._i32_array
+    # lf_pool outputs: 0 or at least n_frames
+    _err(c.lf_pool(F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, 0, 2), 3, F, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_pool(F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, 0, -1), 3, F, F, None), lf.LF_ERR_INVALID_ARG)
+    # selection reads n_kframes pooled frames per (b, h) slice
+    short = lf.Geom(1, 2, 128, 1560, 64, 0, 0, 9)
+    _err(c.lf_select_frames(F, F, short, 75, 10, arr([1]), 1, arr([0]), 1, 1, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_select_blocks(F, F, short, 75, 10, F, 2, 8, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_select(F, F, F, short, 75, 10, arr([1]), 1, arr([0]), 1, 1, 8, F, F, None), lf.LF_ERR_INVALID_ARG)
+    assert "frame_stride" in c.lf_last_error().decode()
 
 
 def test_error_message_is_per_thread():

@@ -81,3 +81,75 @@ def test_token_range_views_equal_packed(dtype):
         assert torch.equal(getattr(packed, name), getattr(views, name)), name
     assert torch.equal(packed.o, big["o"][:, :, off:off + w.lq])
     assert torch.isnan(big["o"][:, :, :off]).all() and torch.isnan(big["o"][:, :, off + w.lq:]).all()
+
+
+def test_cached_sweep_equals_uncached():
+    """The sweep with a pooled-key cache (each chunk pools only its own key frames, the
+    dense first chunk included, and selects over the cached prefix) gives bitwise the
+    lists and outputs of the uncached sweep, and the cache ends up holding the block and
+    frame means of all 21 frames that chunk 7's uncached pooling computes."""
+    from sparse_attention_autoregressive_amd.pipeline import PooledKeyCache
+    s = synth.SWEEP
+    g = lf.Geom(s.B, s.H, s.d, s.tpf, s.bs)
+    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5)
+    log("[sweep-cache] generating layer 5")
+    x = synth.make_sweep_layer(s, 5)
+    dev = torch.device("cuda")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    o_ref, o_c = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
+    sw_ref, sw_c = SweepWorkspace(sp, q.dtype, dev), SweepWorkspace(sp, q.dtype, dev)
+    cache = PooledKeyCache(g, sp.n_frames, dev)
+    cache.k_blk.fill_(float("nan"))
+    cache.k_frm.fill_(float("nan"))
+    stages = []
+    sweep_layer(sw_ref, q, k, v, o_ref)
+    sweep_layer(sw_c, q, k, v, o_c, mark=lambda i, st: stages.append((i, st)), cache=cache)
+    torch.cuda.synchronize()
+    log("[sweep-cache] comparing")
+    assert (1, "pool") in stages and (1, "select") not in stages
+    assert torch.equal(o_ref, o_c)
+    for i in range(2, sp.n_chunks + 1):
+        a, b = sw_ref.chunks[i - 1], sw_c.chunks[i - 1]
+        assert torch.equal(a.q_blk, b.q_blk), i
+        assert torch.equal(a.frames, b.frames), i
+        assert torch.equal(a.blocks, b.blocks), i
+    last = sw_ref.chunks[-1]
+    assert torch.equal(last.k_blk, cache.k_blk) and torch.equal(last.k_frm, cache.k_frm)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "480p_chunk2of7"])
+def test_steady_state_chunk_equals_uncached(name):
+    """One chunk in steady state: packed queries and output, keys and values a prefix of a
+    KV cache with room for more frames (so the query-side and key-side head strides
+    differ), the history's pooled keys in a cache filled beforehand. Pooled queries, the
+    cache's new frames, lists and output equal the uncached call on packed tensors
+    bitwise."""
+    from sparse_attention_autoregressive_amd.pipeline import (PooledKeyCache, Workspace, hsa_chunk,
+                                                              hsa_chunk_cached, new_frames)
+    from support import lib_k_b, plan_of
+    w = synth.WORKLOADS[name]
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    plan = plan_of(w, lib_k_b(w))
+    g = plan.geom
+    ref = Workspace(plan, q.dtype, dev)
+    hsa_chunk(ref, q, k, v)
+    cap_frames = w.n_kframes + 4
+    kc = torch.full((w.B, w.H, cap_frames * w.tpf, w.d), float("nan"), dtype=q.dtype, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    kc[:, :, :w.lk] = k
+    vc[:, :, :w.lk] = v
+    cache = PooledKeyCache(g, cap_frames, dev)
+    cache.k_blk.fill_(float("nan"))
+    cache.k_frm.fill_(float("nan"))
+    f0 = new_frames(plan)
+    lf.lf_pool(kc[:, :, :f0 * w.tpf], g, f0, blk_out=cache.blk(0, f0), frm_out=cache.frm(0, f0))
+    ws = Workspace(plan, q.dtype, dev)
+    hsa_chunk_cached(ws, cache, q, kc[:, :, :w.lk], vc[:, :, :w.lk])
+    torch.cuda.synchronize()
+    assert torch.equal(ref.q_blk, ws.q_blk)
+    assert torch.equal(ref.k_blk, cache.blk(0, w.n_kframes)) and torch.equal(ref.k_frm, cache.frm(0, w.n_kframes))
+    assert torch.isnan(cache.k_frm[:, :, w.n_kframes:]).all()
+    assert torch.equal(ref.frames, ws.frames) and torch.equal(ref.blocks, ws.blocks)
+    assert torch.equal(ref.o, ws.o)
