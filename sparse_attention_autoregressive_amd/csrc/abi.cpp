@@ -211,7 +211,7 @@ lf_status lf_pool(const void* x, lf_dtype dt, lf_geom g, int32_t n_frames, float
   const int n_bpf = n_bpf_of(g);
   const long long BH = static_cast<long long>(g.B) * g.H;
   const long long len = static_cast<long long>(n_frames) * g.tokens_per_frame;
-  if (!fits_int(BH * n_frames * n_bpf) || !fits_int(len))
+  if (!fits_int(BH * n_frames * n_bpf) || !fits_int(BH * n_frames * g.d) || !fits_int(len))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   if (g.head_stride != 0 && g.head_stride < len)
     return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < n_frames*tpf = %lld", fn, g.head_stride, len);
@@ -239,7 +239,7 @@ lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32
   const long long BH = static_cast<long long>(g.B) * g.H;
   const long long lq = static_cast<long long>(n_qframes) * g.tokens_per_frame;
   const long long lk = static_cast<long long>(n_kframes) * g.tokens_per_frame;
-  if (!fits_int(BH * n_kframes * n_bpf) || !fits_int(BH * n_qframes * n_bpf + BH * n_kframes) ||
+  if (!fits_int(BH * (n_qframes + static_cast<long long>(n_kframes)) * n_bpf) || !fits_int(BH * n_kframes * g.d) ||
       !fits_int(lq) || !fits_int(lk))
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   if (g.head_stride != 0 && g.head_stride < lq)

@@ -1,29 +1,28 @@
 // Token compression by mean pooling (Light Forcing summary, execution flow, stage 2):
 // block-level means of queries and keys, frame-level means of keys.
 //
-// One wave pools one block at a time: lane l reads 16-byte chunk l % C of every TL-th
-// token of the block (C = 16-byte chunks per token, TL = 64 / C token lanes),
-// accumulating in fp32; the TL partial sums of each chunk are
-// added across lanes in a fixed order, and the first C lanes write the block mean (the
-// sum divided by the block's true token count). Every input byte is read once, with
-// fully coalesced loads.
+// Block means: one wave pools one block: lane l reads 16-byte chunk l % C of every
+// TL-th token of the block (C = 16-byte chunks per token, TL = 64 / C token lanes),
+// accumulating in fp32, with up to 16 tokens' loads in flight per lane; the TL partial
+// sums of each chunk are added across lanes in a fixed order, and the first C lanes
+// write the block mean (the sum divided by the block's true token count). Every input
+// byte is read once, with fully coalesced loads. The waves of a launch walk one flat
+// list of blocks (all query blocks, then all key blocks), four waves per workgroup, so
+// even a chunk's few frames spread over every CU: a frame's 400 KB is read by about
+// seven CUs instead of one.
 //
-// With frame means requested, a 1024-thread workgroup owns one whole frame: its 16
-// waves take the frame's blocks in turn, keep the running sum of their block sums, and
-// the frame mean is the sum of the waves' sums (added in a fixed order) divided by the
-// frame's token count. Without, a 256-thread workgroup owns four blocks (one per wave),
-// which keeps short tensors (the chunk's queries) spread over every CU. Each lane keeps
-// up to 16 tokens' loads in flight. A combined launch pools a chunk's queries and all
-// keys together (16 query blocks per workgroup); every block is summed by one wave with
-// the same code either way, so results match the separate launches bitwise. Results
-// are deterministic.
+// Frame means: a second, small launch forms each frame's mean from its block means,
+// weighted by the blocks' token counts and added in block order, divided by the frame's
+// token count (a full 64-token block contributes its exact sum). Both launches are the
+// same whether queries and keys are pooled together or apart, so the results match
+// bitwise. Results are deterministic.
 #include "lf_device.h"
 #include "lf_kernels.h"
 
 namespace lf {
 
-constexpr int kPoolWaves = 4;        // waves per workgroup without frame means
-constexpr int kFrameWaves = 16;      // waves per workgroup owning a whole frame
+constexpr int kPoolWaves = 4;        // waves (blocks) per workgroup of the block-mean launch
+constexpr int kFrameThreads = 256;   // threads per workgroup of the frame-mean launch
 
 template <typename T>
 struct Chunk16;
@@ -90,133 +89,117 @@ __device__ __forceinline__ void block_sum(const T* __restrict__ frame, int j, in
   for (int e = 0; e < E; ++e) sum[e] = token_lane_sum<C>(a[e] + b[e]);
 }
 
-// The work of workgroup `wg` (W waves). FRAMES: one workgroup per (b, h, frame), writing
-// block and frame means. Otherwise one workgroup per (b, h, frame, group of W blocks),
-// block means only.
-template <typename T, int D, bool FRAMES, int W>
-__device__ __forceinline__ void pool_part(const T* __restrict__ x, float* __restrict__ blk, float* __restrict__ frm,
-                                          int n_frames, int tpf, int bs, int n_bpf, long long x_stride,
-                                          int out_stride, int wg, float (*fs)[D]) {
+// One tensor's share of a block-mean launch: n_blocks = BH * n_frames * n_bpf blocks,
+// the (b, h) slices x_stride tokens apart in x and out_stride frames apart in blk.
+template <typename T>
+struct PoolJob {
+  const T* x;
+  float* blk;
+  long long x_stride;
+  int n_frames, out_stride, n_blocks;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void pool_block(const PoolJob<T>& p, int b, int tpf, int bs, int n_bpf, int lane) {
   constexpr int E = Chunk16<T>::E;
   constexpr int C = D / E;
-  const int groups = FRAMES ? 1 : (n_bpf + W - 1) / W;
-  const int grp = wg % groups;
-  const int bf = wg / groups;                         // bh * n_frames + f
-  const int bh = bf / n_frames, f = bf - bh * n_frames;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const T* frame = x + (static_cast<size_t>(bh) * x_stride + static_cast<size_t>(f) * tpf) * D;
-  const size_t of = static_cast<size_t>(bh) * out_stride + f;   // output frame slot
-  float* blk_row = blk + of * n_bpf * D;
-
-  float fsum[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) fsum[e] = 0.f;
-  const int j0 = FRAMES ? wave : grp * W + wave;
-  const int dj = FRAMES ? W : n_bpf;               // without frames: one block per wave
-  for (int j = j0; j < n_bpf; j += dj) {
-    const int len = min(bs, tpf - j * bs);
-    float sum[E];
-    block_sum<T, D>(frame, j, bs, len, lane, sum);
-    if (lane < C) {
-      const float inv = 1.0f / static_cast<float>(len);
-      float* out = blk_row + static_cast<size_t>(j) * D + lane * E;
-#pragma unroll
-      for (int e = 0; e < E; e += 4)
-        *reinterpret_cast<float4*>(out + e) =
-            make_float4(sum[e] * inv, sum[e + 1] * inv, sum[e + 2] * inv, sum[e + 3] * inv);
-#pragma unroll
-      for (int e = 0; e < E; ++e) fsum[e] += sum[e];
-    }
-  }
-  if (!FRAMES) return;
+  const int bf = b / n_bpf, j = b - bf * n_bpf;     // bf = bh * n_frames + f
+  const int bh = bf / p.n_frames, f = bf - bh * p.n_frames;
+  const T* frame = p.x + (static_cast<size_t>(bh) * p.x_stride + static_cast<size_t>(f) * tpf) * D;
+  const int len = min(bs, tpf - j * bs);
+  float sum[E];
+  block_sum<T, D>(frame, j, bs, len, lane, sum);
   if (lane < C) {
+    const float inv = 1.0f / static_cast<float>(len);
+    float* out = p.blk + ((static_cast<size_t>(bh) * p.out_stride + f) * n_bpf + j) * D + lane * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) fs[wave][lane * E + e] = fsum[e];
-  }
-  __syncthreads();
-  if (threadIdx.x < D) {
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) t += fs[w][threadIdx.x];
-    frm[of * D + threadIdx.x] = t / static_cast<float>(tpf);
+    for (int e = 0; e < E; e += 4)
+      *reinterpret_cast<float4*>(out + e) =
+          make_float4(sum[e] * inv, sum[e + 1] * inv, sum[e + 2] * inv, sum[e + 3] * inv);
   }
 }
 
-template <typename T, int D, bool FRAMES>
-__global__ void __launch_bounds__((FRAMES ? kFrameWaves : kPoolWaves) * kWave) pool_kernel(
-    const T* __restrict__ x, float* __restrict__ blk, float* __restrict__ frm, int n_frames, int tpf, int bs,
-    int n_bpf, long long x_stride, int out_stride) {
-  constexpr int W = FRAMES ? kFrameWaves : kPoolWaves;
-  __shared__ __attribute__((aligned(16))) float fs[W][D];
-  pool_part<T, D, FRAMES, W>(x, blk, frm, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blockIdx.x, fs);
-}
-
-// Queries (block means) and keys (block and frame means) in one launch: the first n_qwg
-// workgroups pool query blocks, 16 per workgroup, the rest one key frame each.
+// Wave w of the grid pools block w of the list "a's blocks, then b's blocks".
 template <typename T, int D>
-__global__ void __launch_bounds__(kFrameWaves * kWave) pool_qk_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ q_blk, float* __restrict__ k_blk,
-    float* __restrict__ k_frm, int n_qframes, int n_kframes, int tpf, int bs, int n_bpf, long long q_stride,
-    long long k_stride, int k_out_stride, int n_qwg) {
-  __shared__ __attribute__((aligned(16))) float fs[kFrameWaves][D];
-  const int wg = blockIdx.x;
-  if (wg < n_qwg)
-    pool_part<T, D, false, kFrameWaves>(q, q_blk, nullptr, n_qframes, tpf, bs, n_bpf, q_stride, n_qframes, wg, fs);
-  else
-    pool_part<T, D, true, kFrameWaves>(k, k_blk, k_frm, n_kframes, tpf, bs, n_bpf, k_stride, k_out_stride,
-                                       wg - n_qwg, fs);
+__global__ void __launch_bounds__(kPoolWaves * kWave) block_mean_kernel(PoolJob<T> a, PoolJob<T> b, int tpf, int bs,
+                                                                        int n_bpf) {
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kPoolWaves + threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  if (w < a.n_blocks)
+    pool_block<T, D>(a, w, tpf, bs, n_bpf, lane);
+  else if (w - a.n_blocks < b.n_blocks)
+    pool_block<T, D>(b, w - a.n_blocks, tpf, bs, n_bpf, lane);
+}
+
+// Thread (frame, channel): the frame mean from the frame's block means, each weighted
+// by its token count, added in block order. n_slices_frames = BH * n_frames.
+template <int D>
+__global__ void __launch_bounds__(kFrameThreads) frame_mean_kernel(const float* __restrict__ blk,
+                                                                   float* __restrict__ frm, int n_slice_frames,
+                                                                   int n_frames, int out_stride, int tpf, int bs,
+                                                                   int n_bpf) {
+  const int t = blockIdx.x * kFrameThreads + threadIdx.x;
+  const int bf = t / D, c = t % D;
+  if (bf >= n_slice_frames) return;
+  const int bh = bf / n_frames, f = bf - bh * n_frames;
+  const size_t slot = static_cast<size_t>(bh) * out_stride + f;
+  const float* row = blk + slot * n_bpf * D + c;
+  float s = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < n_bpf; ++j) s += row[static_cast<size_t>(j) * D] * static_cast<float>(min(bs, tpf - j * bs));
+  frm[slot * D + c] = s / static_cast<float>(tpf);
 }
 
 template <typename T, int D>
-static hipError_t launch_pool_t(const void* x, int BH, int n_frames, int tpf, int bs, int n_bpf,
-                                long long x_stride, int out_stride, float* blk, float* frm, hipStream_t st) {
-  const unsigned frames = static_cast<unsigned>(BH) * n_frames;
-  if (frm != nullptr) {
-    hipLaunchKernelGGL((pool_kernel<T, D, true>), dim3(frames), dim3(kFrameWaves * kWave), 0, st,
-                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride, out_stride);
-  } else {
-    const unsigned groups = (n_bpf + kPoolWaves - 1) / kPoolWaves;
-    hipLaunchKernelGGL((pool_kernel<T, D, false>), dim3(frames * groups), dim3(kPoolWaves * kWave), 0, st,
-                       static_cast<const T*>(x), blk, frm, n_frames, tpf, bs, n_bpf, x_stride, out_stride);
-  }
+static hipError_t launch_t(PoolJob<T> a, PoolJob<T> b, float* frm, int BH, int tpf, int bs, int n_bpf,
+                           hipStream_t st) {
+  const unsigned waves = static_cast<unsigned>(a.n_blocks) + static_cast<unsigned>(b.n_blocks);
+  hipLaunchKernelGGL((block_mean_kernel<T, D>), dim3((waves + kPoolWaves - 1) / kPoolWaves),
+                     dim3(kPoolWaves * kWave), 0, st, a, b, tpf, bs, n_bpf);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (frm == nullptr) return hipSuccess;
+  // frame means of b (the keys)
+  const int n_sf = BH * b.n_frames;
+  const unsigned grid = static_cast<unsigned>((static_cast<long long>(n_sf) * D + kFrameThreads - 1) / kFrameThreads);
+  hipLaunchKernelGGL((frame_mean_kernel<D>), dim3(grid), dim3(kFrameThreads), 0, st, b.blk, frm, n_sf, b.n_frames,
+                     b.out_stride, tpf, bs, n_bpf);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t launch_pool_qk_t(const void* q, const void* k, int BH, int n_qframes, int n_kframes, int tpf,
-                                   int bs, int n_bpf, long long q_stride, long long k_stride, int k_out_stride,
-                                   float* q_blk, float* k_blk, float* k_frm, hipStream_t st) {
-  const int n_qwg = BH * n_qframes * ((n_bpf + kFrameWaves - 1) / kFrameWaves);
-  const unsigned grid = static_cast<unsigned>(n_qwg) + static_cast<unsigned>(BH) * n_kframes;
-  hipLaunchKernelGGL((pool_qk_kernel<T, D>), dim3(grid), dim3(kFrameWaves * kWave), 0, st,
-                     static_cast<const T*>(q), static_cast<const T*>(k), q_blk, k_blk, k_frm, n_qframes, n_kframes,
-                     tpf, bs, n_bpf, q_stride, k_stride, k_out_stride, n_qwg);
-  return hipGetLastError();
+template <typename T>
+static PoolJob<T> job(const void* x, float* blk, int BH, int n_frames, int n_bpf, long long x_stride,
+                      int out_stride) {
+  return PoolJob<T>{static_cast<const T*>(x), blk, x_stride, n_frames, out_stride, BH * n_frames * n_bpf};
+}
+
+template <typename T>
+static hipError_t launch_d(int d, PoolJob<T> a, PoolJob<T> b, float* frm, int BH, int tpf, int bs, int n_bpf,
+                           hipStream_t st) {
+  return d == 128 ? launch_t<T, 128>(a, b, frm, BH, tpf, bs, n_bpf, st)
+                  : launch_t<T, 64>(a, b, frm, BH, tpf, bs, n_bpf, st);
 }
 
 hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH, int n_qframes, int n_kframes,
                           int tpf, int bs, int n_bpf, long long q_stride, long long k_stride, int k_out_stride,
                           float* q_blk, float* k_blk, float* k_frm, hipStream_t st) {
-  if (bf16) {
-    return d == 128 ? launch_pool_qk_t<__bf16, 128>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
-                                                    k_stride, k_out_stride, q_blk, k_blk, k_frm, st)
-                    : launch_pool_qk_t<__bf16, 64>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
-                                                   k_stride, k_out_stride, q_blk, k_blk, k_frm, st);
-  }
-  return d == 128 ? launch_pool_qk_t<float, 128>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride,
-                                                 k_stride, k_out_stride, q_blk, k_blk, k_frm, st)
-                  : launch_pool_qk_t<float, 64>(q, k, BH, n_qframes, n_kframes, tpf, bs, n_bpf, q_stride, k_stride,
-                                                k_out_stride, q_blk, k_blk, k_frm, st);
+  if (bf16)
+    return launch_d<__bf16>(d, job<__bf16>(q, q_blk, BH, n_qframes, n_bpf, q_stride, n_qframes),
+                            job<__bf16>(k, k_blk, BH, n_kframes, n_bpf, k_stride, k_out_stride), k_frm, BH, tpf, bs,
+                            n_bpf, st);
+  return launch_d<float>(d, job<float>(q, q_blk, BH, n_qframes, n_bpf, q_stride, n_qframes),
+                         job<float>(k, k_blk, BH, n_kframes, n_bpf, k_stride, k_out_stride), k_frm, BH, tpf, bs,
+                         n_bpf, st);
 }
 
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
                        int n_bpf, long long x_stride, int out_stride, float* blk, float* frm, hipStream_t st) {
-  if (bf16) {
-    return d == 128 ? launch_pool_t<__bf16, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st)
-                    : launch_pool_t<__bf16, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st);
-  }
-  return d == 128 ? launch_pool_t<float, 128>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st)
-                  : launch_pool_t<float, 64>(x, BH, n_frames, tpf, bs, n_bpf, x_stride, out_stride, blk, frm, st);
+  // a single tensor rides in the second slot (the one whose frame means are formed)
+  if (bf16)
+    return launch_d<__bf16>(d, PoolJob<__bf16>{nullptr, nullptr, 0, 1, 1, 0},
+                            job<__bf16>(x, blk, BH, n_frames, n_bpf, x_stride, out_stride), frm, BH, tpf, bs, n_bpf,
+                            st);
+  return launch_d<float>(d, PoolJob<float>{nullptr, nullptr, 0, 1, 1, 0},
+                         job<float>(x, blk, BH, n_frames, n_bpf, x_stride, out_stride), frm, BH, tpf, bs, n_bpf, st);
 }
 
 }  // namespace lf
