@@ -112,6 +112,29 @@ def hold_stream(ms: float = 50.0):
     torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))
 
 
+def mfma_ceiling(n_wg: int = 512, iters: int = 20000, reps: int = 3):
+    """Measured dense bf16 matrix-core rate (register-only MFMA chains, 2 waves per SIMD on
+    every CU) and the shader clock under that load; best of `reps` launches."""
+    dev = torch.device("cuda")
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    flops = n_wg * 16.0 * iters * 32768.0
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lf.lf_probe_mfma_bf16(n_wg, iters, sink, clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        cyc, ticks = clocks.tolist()
+        ghz = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else float("nan")
+        if best is None or tf > best[0]:
+            best = (tf, ghz)
+    return {"tflops": round(best[0], 1), "clock_ghz": round(best[1], 3),
+            "what": f"register-only v_mfma_f32_32x32x16_bf16 chains, {n_wg} x 4 waves, {iters} x 4 MFMAs per wave"}
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -228,6 +251,7 @@ def main():
     ms_per_step, mean_us, med_us = timed(False)
     ss_ms, ss_mean, ss_med = timed(True)
 
+    ceiling = mfma_ceiling()
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
     t_attn = mean_us[2] * 1e-6
@@ -298,6 +322,7 @@ def main():
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_of(w.name)},
+        "mfma_ceiling": {**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
@@ -380,6 +405,7 @@ def bench_sweep(args):
 
     ms_per_step, stage_us, chunk_us = timed(False)
     ss_ms, ss_stage, ss_chunk = timed(True)
+    ceiling = mfma_ceiling()
     t_attn = stage_us["attn"] * 1e-6
     attn_tflops = f_active / t_attn / 1e12
     cpu = None
@@ -428,6 +454,7 @@ def bench_sweep(args):
         "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_of(s.name)},
+        "mfma_ceiling": {**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -16,8 +16,7 @@ import torch
 
 __all__ = ["Geom", "LfError", "lf_abi_version", "lf_cag_schedule", "lf_block_budget",
            "lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
-           "library_path",
-           "n_bpf"]
+           "lf_probe_mfma_bf16", "library_path", "n_bpf"]
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_INFEASIBLE, LF_ERR_HIP = range(5)
 LF_FP32, LF_BF16 = 0, 1
@@ -97,6 +96,7 @@ def _load():
         "lf_select_blocks": [vp, vp, Geom, i32, i32, vp, i32, i32, vp, vp],
         "lf_select": [vp, vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, i32, vp, vp, vp],
         "lf_sparse_attn": [vp, vp, vp, vp, i32, Geom, i32, i32, vp, i32, f32, vp],
+        "lf_probe_mfma_bf16": [i32, i32, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -314,3 +314,14 @@ def lf_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geom, n
                               _dtype_code(q), ga, n_qframes, n_kframes, _dev(blocks, "blocks"),
                               blocks.shape[-1], float(scale), _stream(q)))
     return out
+
+
+def lf_probe_mfma_bf16(n_wg: int, iters: int, sink: torch.Tensor, clocks: torch.Tensor) -> None:
+    """Enqueues the dense bf16 MFMA loop (include/lf_probe.h) on the current stream:
+    n_wg * 16 * iters * 32768 FLOPs; sink: float32 [n_wg * 256], clocks: int64 [2] (shader
+    cycles and 100 MHz ticks of one wave's loop)."""
+    if sink.dtype != torch.float32 or sink.numel() < n_wg * 256:
+        raise ValueError("sink must be float32 with n_wg * 256 entries")
+    if clocks.dtype != torch.int64 or clocks.numel() < 2:
+        raise ValueError("clocks must be int64 with 2 entries")
+    _check(_load().lf_probe_mfma_bf16(n_wg, iters, _dev(sink, "sink"), _dev(clocks, "clocks"), _stream(sink)))

@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "liblf.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "pool.hip", "select.hip", "attn.hip"]
+SOURCES = ["abi.cpp", "pool.hip", "select.hip", "attn.hip", "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -10,6 +10,7 @@
 #include <cstdio>
 
 #include "../../include/lf.h"
+#include "../../include/lf_probe.h"
 #include "lf_kernels.h"
 
 namespace {
@@ -346,6 +347,18 @@ lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, l
   pending_error();
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(dt == LF_BF16 ? lf::launch_attn_bf16(a, g.d, st) : lf::launch_attn_f32(a, g.d, st), fn);
+}
+
+lf_status lf_probe_mfma_bf16(int32_t n_wg, int32_t iters, float* sink, int64_t* clocks, void* stream) {
+  const char* fn = "lf_probe_mfma_bf16";
+  if (n_wg < 1 || iters < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_wg and iters must be >= 1", fn);
+  if (!sink || !clocks) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u) || (reinterpret_cast<uintptr_t>(clocks) & 7u))
+    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  pending_error();
+  return hip_status(lf::launch_mfma_probe(n_wg, iters, sink, reinterpret_cast<long long*>(clocks),
+                                          static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 }  // extern "C"

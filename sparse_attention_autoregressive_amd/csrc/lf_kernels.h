@@ -62,4 +62,7 @@ struct AttnArgs {
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t st);
 
+// Dense bf16 MFMA loop of n_wg 4-wave workgroups (measurement aid).
+hipError_t launch_mfma_probe(int n_wg, int iters, float* sink, long long* clocks, hipStream_t st);
+
 }  // namespace lf

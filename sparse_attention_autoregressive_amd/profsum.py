@@ -32,7 +32,7 @@ def source_sha(path: str = ATTN_SOURCE) -> str:
 
 
 def _short(name: str) -> str:
-    n = re.sub(r"\(.*", "", name)
+    n = re.sub(r"\(.*", "", name.replace("(anonymous namespace)", "anon"))
     return n if len(n) < 90 else n[:87] + "..."
 
 

@@ -18,15 +18,20 @@ pytestmark = pytest.mark.skipif(lib_missing, reason="liblf.so not built")
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "lf.h")).read()
-    return sorted(set(re.findall(r"\b(lf_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"\b(lf_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(lf.library_path())
     names = _declared()
     assert {"lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
-            "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version"} <= set(names)
+            "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version",
+            "lf_probe_mfma_bf16"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lf.lf_abi_version() == 3
@@ -241,3 +246,11 @@ def test_error_message_is_per_thread():
     t.join()
     assert seen["msg"] == ""
     assert "lf_pool" in c.lf_last_error().decode()
+
+
+def test_probe_validation():
+    c = _c()
+    _err(c.lf_probe_mfma_bf16(0, 10, FAKE, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_mfma_bf16(4, 0, FAKE, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_mfma_bf16(4, 10, FAKE, FAKE + 4, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_mfma_bf16(4, 10, None, FAKE, None), lf.LF_ERR_INVALID_ARG)
