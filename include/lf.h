@@ -89,7 +89,9 @@ int32_t lf_abi_version(void);
  *   any common unit (for equal chunks against a growing cache, F_i is proportional to i).
  * alpha (host, n_chunks entries, or NULL): the alpha_i weights. NULL selects
  *   alpha_i = 1/sqrt(i*T), this library's reading of "alpha_i proportional to 1/sqrt(T),
- *   the noise level reached by chunk i". alpha_1 is ignored.
+ *   the noise level reached by chunk i". alpha_1 is ignored. A constant alpha makes
+ *   every s_i (i > 1) equal: the uniform allocation CAG is compared against, under the
+ *   same FLOP budget (163.com article on Light Forcing, section 2).
  * Outputs (host): s_out[n_chunks], *beta_out.
  * Errors: LF_ERR_INVALID_ARG for bad sizes/pointers/values; LF_ERR_INFEASIBLE when the
  *   solution has beta < 0 or some s_i outside [0, 1) (nothing is clamped).

@@ -108,6 +108,24 @@ def cag_schedule(n_chunks: int, T: int, s_base: float, s_target: float,
     return s, beta
 
 
+def uniform_schedule(n_chunks: int, s_target: float, chunk_flops: Sequence[float]):
+    """The allocation Chunk-Aware Growth is compared against (163.com article, section 2:
+    the same FLOP budget spread uniformly; gist.science technical summary, section 1: the
+    isolated treatment of chunks): chunk 1 dense, every later chunk at one sparsity s',
+    fixed by the same budget as CAG. Solving F_1 + (1 - s') * sum_{i>1} F_i =
+    (1 - s_target) * sum_i F_i for s' gives s' = s_target * sum_i F_i / sum_{i>1} F_i.
+    Raises ValueError if s' is not in [0, 1)."""
+    F = np.asarray(chunk_flops, dtype=np.float64)
+    if F.shape != (n_chunks,) or n_chunks < 2:
+        raise ValueError("chunk_flops must have n_chunks >= 2 entries")
+    sp = s_target * F.sum() / F[1:].sum()
+    if not (0.0 <= sp < 1.0):
+        raise ValueError(f"infeasible uniform target: s'={sp}")
+    s = np.full(n_chunks, sp)
+    s[0] = 0.0
+    return s
+
+
 def block_budget(s: float, n_kb: int, W_f: int, n_bpf: int) -> int:
     """Reading R4/R17 (the pages' per-chunk top-k table is not available): keep
     round-half-up((1 - s) * n_kb / W_f) blocks per selected frame, clamped to

@@ -208,12 +208,19 @@ class SweepPlan:
 
 
 def plan_sweep(g: Geom, n_chunks: int, frames_per_chunk: int, k_f: int, T: int, s_base: float,
-               s_target: float, scale: float, sink: Sequence[int] = (0,)) -> SweepPlan:
-    """CAG schedule (once per clip) and per-chunk plans. The FLOP weight of chunk i is its
-    dense attention work, query tokens times key tokens (proportional to i)."""
+               s_target: float, scale: float, sink: Sequence[int] = (0,), schedule: str = "cag") -> SweepPlan:
+    """Sparsity schedule (once per clip) and per-chunk plans. The FLOP weight of chunk i is
+    its dense attention work, query tokens times key tokens (proportional to i).
+    schedule "cag": Chunk-Aware Growth. "uniform": the allocation CAG is compared against
+    (163.com article, section 2), chunk 1 dense and one sparsity for every later chunk
+    under the same FLOP budget; it is the CAG solution for a constant alpha, so it comes
+    from the same library call."""
     fpc, tpf, nb = frames_per_chunk, g.tokens_per_frame, n_bpf(g)
     flops = [float(fpc * tpf * fpc * i * tpf) for i in range(1, n_chunks + 1)]
-    s, beta = lf_cag_schedule(n_chunks, T, s_base, s_target, flops)
+    if schedule not in ("cag", "uniform"):
+        raise ValueError(f"unknown schedule {schedule!r}")
+    alpha = [1.0] * n_chunks if schedule == "uniform" else None
+    s, beta = lf_cag_schedule(n_chunks, T, s_base, s_target, flops, alpha)
     sp = SweepPlan(g, fpc, s, beta)
     for i in range(1, n_chunks + 1):
         cur = list(range(fpc * (i - 1), fpc * i))

@@ -50,6 +50,9 @@ class Workload:
     s_base: float = 0.95
     s_target: float = 0.80
     seed: int = 0
+    # Sparsity allocation over chunks: "cag" (Chunk-Aware Growth) or "uniform" (every
+    # chunk after the first at one sparsity, same FLOP budget).
+    schedule: str = "cag"
 
     @property
     def n_qframes(self) -> int:
@@ -132,8 +135,9 @@ class Sweep:
     def seed(self, layer: int) -> int:
         return self.seed_base + layer
 
-    def chunk(self, i: int, layer: int = 0) -> Workload:
-        """Workload of chunk i (1-based) in one layer; k_b left to the CAG budget."""
+    def chunk(self, i: int, layer: int = 0, schedule: str = "cag") -> Workload:
+        """Workload of chunk i (1-based) in one layer; k_b left to the budget of the
+        schedule ("cag" or "uniform")."""
         fpc = self.frames_per_chunk
         cur = _frames(fpc * (i - 1), fpc * i)
         mem = _frames(1, fpc * (i - 1)) if i > 1 else ()
@@ -143,7 +147,7 @@ class Sweep:
             dtype=self.dtype, tpf=self.tpf, bs=self.bs, n_kframes=fpc * i,
             current=cur, sink=(0,), recent=(), mem=mem, k_f=self.k_f, k_b=None,
             q_pool=pool, chunk_index=i, n_chunks=self.n_chunks, T=self.T,
-            s_base=self.s_base, s_target=self.s_target, seed=self.seed(layer),
+            s_base=self.s_base, s_target=self.s_target, seed=self.seed(layer), schedule=schedule,
         )
 
 

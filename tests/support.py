@@ -51,7 +51,8 @@ def lib_k_b(w: synth.Workload) -> int:
     """k_b as the library derives it (CAG schedule + budget rule) unless given."""
     if w.k_b is not None:
         return w.k_b
-    s, _ = lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
+    alpha = [1.0] * w.n_chunks if w.schedule == "uniform" else None
+    s, _ = lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w), alpha)
     nb = -(-w.tpf // w.bs)
     W_f = len(w.forced) + min(w.k_f, len(w.mem))
     return lf.lf_block_budget(s[w.chunk_index - 1], w.n_kframes * nb, W_f, nb)
@@ -60,7 +61,10 @@ def lib_k_b(w: synth.Workload) -> int:
 def oracle_k_b(w: synth.Workload) -> int:
     if w.k_b is not None:
         return w.k_b
-    s, _ = oracle.cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
+    if w.schedule == "uniform":
+        s = oracle.uniform_schedule(w.n_chunks, w.s_target, chunk_flops(w))
+    else:
+        s, _ = oracle.cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
     nb = -(-w.tpf // w.bs)
     W_f = len(w.forced) + min(w.k_f, len(w.mem))
     return oracle.block_budget(s[w.chunk_index - 1], w.n_kframes * nb, W_f, nb)

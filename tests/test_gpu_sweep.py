@@ -1,8 +1,8 @@
 """GPU parity of the Chunk-Aware Growth sweep (7 chunks of a 480p clip, one layer at a
 time), run as the sweep driver runs it: token-range views of per-layer Q/K/V/O tensors
-that hold the whole clip. On layers 0 and 29 every chunk's masks (every row) and
-outputs (sampled rows; the dense first chunk included) are compared with the oracle run
-on that chunk's slice of the layer."""
+that hold the whole clip. On layers 0 and 29 (CAG schedule) and layer 3 (the uniform
+allocation) every chunk's masks (every row) and outputs (sampled rows; the dense first
+chunk included) are compared with the oracle run on that chunk's slice of the layer."""
 import numpy as np
 import pytest
 import torch
@@ -15,11 +15,12 @@ from support import compare_attention, compare_masks, log, oracle_k_b, run_oracl
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("layer", [0, 29])
-def test_sweep_layer_parity(layer):
+@pytest.mark.parametrize("layer,schedule", [(0, "cag"), (29, "cag"), (3, "uniform")])
+def test_sweep_layer_parity(layer, schedule):
     s = synth.SWEEP
     g = lf.Geom(s.B, s.H, s.d, s.tpf, s.bs)
-    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5)
+    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5,
+                    schedule=schedule)
     log(f"[sweep] layer {layer}: generating inputs")
     x = synth.make_sweep_layer(s, layer)
     dev = torch.device("cuda")
@@ -34,7 +35,7 @@ def test_sweep_layer_parity(layer):
     o_np = o.float().cpu().numpy()
     tpf, fpc = s.tpf, s.frames_per_chunk
     for i, p in enumerate(sp.chunks, 1):
-        w = s.chunk(i, layer)
+        w = s.chunk(i, layer, schedule)
         assert p.k_b == oracle_k_b(w)
         a, b = (i - 1) * fpc * tpf, i * fpc * tpf
         qi, ki, vi = q64[:, :, a:b], k64[:, :, :b], v64[:, :, :b]

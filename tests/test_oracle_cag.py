@@ -90,3 +90,21 @@ def test_block_budget_rule_and_sweep_table():
     assert oracle.block_budget(0.5, 10, 2, 25) == 3          # x = 2.5 -> 3
     assert oracle.block_budget(0.99, 10, 8, 25) == 1         # clamp low
     assert oracle.block_budget(0.0, 500, 2, 25) == 25        # clamp high
+
+
+def test_uniform_schedule_pins():
+    """The uniform allocation: a worked case by hand, the budget identity, and agreement
+    with the CAG solver at a constant alpha (where CAG's growth term vanishes)."""
+    # F = (1, 2), target 0.5: keep 1.5 = 1 + 2 (1 - s')  ->  s' = 0.75
+    assert np.allclose(oracle.uniform_schedule(2, 0.5, [1.0, 2.0]), [0.0, 0.75], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(3)
+    for n in (3, 7, 12):
+        F = rng.uniform(0.5, 2.0, n).cumsum()
+        for st in (0.3, 0.6, 0.8):
+            s = oracle.uniform_schedule(n, st, F)
+            assert s[0] == 0.0 and np.ptp(s[1:]) == 0.0
+            assert abs(np.dot(F, 1 - s) - (1 - st) * F.sum()) < 1e-12 * F.sum()
+            s_c, beta = oracle.cag_schedule(n, 4, 0.99, st, F, alpha=np.ones(n))
+            assert np.allclose(s_c, s, rtol=0, atol=1e-12) and beta >= 0
+    with pytest.raises(ValueError):
+        oracle.uniform_schedule(3, 0.95, [1.0, 1.0, 1.0])     # s' = 1.425

@@ -44,3 +44,26 @@ def test_first_chunk_dense_and_target_met():
     # budgets never shrink as the cache grows (CAG sparsity grows slower than the cache)
     kb = [p.k_b for p in sp.chunks[1:]]
     assert kb == sorted(kb)
+
+
+def test_uniform_plan_matches_oracle_and_budget():
+    """The uniform allocation (chunk 1 dense, one sparsity after it) from the library's
+    CAG call with a constant alpha equals the oracle's closed form, keeps the same FLOP
+    budget as CAG, and its per-chunk block budgets follow the same rule."""
+    s = synth.SWEEP
+    g = lf.Geom(s.B, s.H, s.d, s.tpf, s.bs)
+    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5,
+                    schedule="uniform")
+    flops = np.array([float(3 * s.tpf * 3 * i * s.tpf) for i in range(1, s.n_chunks + 1)])
+    s_or = oracle.uniform_schedule(s.n_chunks, s.s_target, flops)
+    assert np.allclose(sp.s, s_or, rtol=0, atol=1e-12)
+    assert sp.s[0] == 0.0 and np.ptp(sp.s[1:]) < 1e-12
+    assert abs(np.dot(flops, 1 - np.asarray(sp.s)) - (1 - s.s_target) * flops.sum()) < 1e-9 * flops.sum()
+    nb = -(-s.tpf // s.bs)
+    for i, p in enumerate(sp.chunks, 1):
+        w = s.chunk(i, schedule="uniform")
+        W_f = len(w.forced) + min(w.k_f, len(w.mem))
+        assert p.k_b == oracle.block_budget(s_or[i - 1], w.n_kframes * nb, W_f, nb)
+    with pytest.raises(ValueError):
+        plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5,
+                   schedule="linear")
