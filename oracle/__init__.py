@@ -5,8 +5,8 @@ CPU-baseline leg, never by the product path. Shares no code with the HIP library
 """
 from .hsa import (attn_flops, block_budget, block_geometry, block_mask, block_tokens,
                   cag_alpha, cag_schedule, uniform_schedule, dense_attn, hsa, pool_blocks, pool_frames,
-                  select_blocks, select_frames, sparse_attn)
+                  select_blocks, select_blocks_1d, select_frames, sparse_attn)
 
 __all__ = ["attn_flops", "block_budget", "block_geometry", "block_mask", "block_tokens",
            "cag_alpha", "cag_schedule", "uniform_schedule", "dense_attn", "hsa", "pool_blocks", "pool_frames",
-           "select_blocks", "select_frames", "sparse_attn"]
+           "select_blocks", "select_blocks_1d", "select_frames", "sparse_attn"]

@@ -32,7 +32,8 @@ turning s_i into a per-frame block count (R4, R17); frame-aligned ragged blocks 
 R6); memory set = key frames not forced (R7); per-head masks (R8); per-frame block
 top-k also inside forced frames (R9); raw inner products (R10); ties broken toward the
 lower index (R11); k >= candidates keeps all (R12); no causal mask (R13); softmax over
-the selected tokens only, scale 1/sqrt(d) (R14); ascending fixed-width lists (R15).
+the selected tokens only, scale 1/sqrt(d) (R14); ascending fixed-width lists (R15); the
+single-level comparison variant keeps no frame always (R23).
 
 Parity status: the pages print no worked example and no reference output, so the
 whole pipeline is pinned by closed forms, invariants, library special cases and brute
@@ -219,6 +220,30 @@ def select_blocks(q_blk: np.ndarray, k_blk: np.ndarray, frames: np.ndarray, n_bp
                     J, gaps[b, h, r, t] = _top(o_r, js, k_b)
                     ids.extend(int(tau) * n_bpf + np.sort(J))
                 blocks[b, h, r] = ids
+    return blocks, gaps
+
+
+def select_blocks_1d(q_blk: np.ndarray, k_blk: np.ndarray, K: int):
+    """The single-granularity selection HSA is contrasted with (Light Forcing summary,
+    novelty paragraph: earlier dynamic sparse attention picks blocks at one level only;
+    163.com article, ablation section: the "1D" variant): every key block j of the prefix
+    is scored o_r(j) = <q~_r, k~_j>, and the top-min(K, n_kb) by (-o, j) form the row's
+    list, ascending. There is no frame stage and no always-kept frame (reading R23).
+
+    q_blk [B,H,n_qb,d], k_blk [B,H,n_kb,d]. Returns (blocks [B,H,n_qb,min(K,n_kb)] int64,
+    gaps [B,H,n_qb] of o at the cut)."""
+    B, H, n_qb, d = q_blk.shape
+    n_kb = k_blk.shape[2]
+    ke = min(K, n_kb)
+    blocks = np.empty((B, H, n_qb, ke), dtype=np.int64)
+    gaps = np.full((B, H, n_qb), math.inf)
+    ids = np.arange(n_kb, dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(n_qb):
+                o_r = k_blk[b, h] @ q_blk[b, h, r]
+                J, gaps[b, h, r] = _top(o_r, ids, K)
+                blocks[b, h, r] = np.sort(J)
     return blocks, gaps
 
 

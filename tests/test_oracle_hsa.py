@@ -270,3 +270,35 @@ def test_attn_flops_counts():
     dense, active = oracle.attn_flops(blocks, 10, 4, 2)
     assert dense == 10 * 20
     assert active == 4 * (4 + 2) + 4 * (4 + 2) + 2 * (4 + 4)
+
+
+def test_one_level_selection_pins():
+    """Single-level block top-k: a worked case by hand (ties to the lower id), K at or
+    above the block count keeps everything, brute force over all K-subsets on tiny
+    inputs, and the reduction to HSA's block stage when the prefix is one frame."""
+    q = np.zeros((1, 1, 1, 2))
+    q[..., 0] = 1.0
+    kb = np.zeros((1, 1, 4, 2))
+    kb[0, 0, :, 0] = [0.5, 2.0, -1.0, 2.0]            # scores 0.5, 2, -1, 2
+    blocks, gaps = oracle.select_blocks_1d(q, kb, 2)
+    assert blocks.tolist() == [[[[1, 3]]]] and gaps[0, 0, 0] == 1.5
+    assert oracle.select_blocks_1d(q, kb, 3)[0].tolist() == [[[[0, 1, 3]]]]
+    assert oracle.select_blocks_1d(q, kb, 9)[0].tolist() == [[[[0, 1, 2, 3]]]]
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        n_kb, d, K = int(rng.integers(3, 8)), 4, int(rng.integers(1, 5))
+        q = rng.standard_normal((1, 1, 1, d))
+        kb = rng.standard_normal((1, 1, n_kb, d))
+        got = oracle.select_blocks_1d(q, kb, K)[0][0, 0, 0].tolist()
+        s = kb[0, 0] @ q[0, 0, 0]
+        best = max(itertools.combinations(range(n_kb), min(K, n_kb)), key=lambda c: (sum(s[list(c)]), [-i for i in c]))
+        assert got == sorted(best)
+    # one frame of n_bpf blocks: the same list as the block stage with T_r = {0}
+    n_bpf, d = 6, 8
+    q = rng.standard_normal((1, 2, 3, d))
+    kb = rng.standard_normal((1, 2, n_bpf, d))
+    frames = np.zeros((1, 2, 3, 1), dtype=np.int64)
+    for K in (1, 3, 6):
+        two, _ = oracle.select_blocks(q, kb, frames, n_bpf, K)
+        one, _ = oracle.select_blocks_1d(q, kb, K)
+        assert np.array_equal(one, two)
