@@ -37,8 +37,9 @@ import synth  # noqa: E402
 import sparse_attention_autoregressive_amd as lf  # noqa: E402
 from sparse_attention_autoregressive_amd.profsum import read_traffic  # noqa: E402
 from sparse_attention_autoregressive_amd.pipeline import (ChunkPlan, PooledKeyCache, SweepWorkspace,  # noqa: E402
-                                                          Workspace, attend, new_frames, plan_sweep, pool,
-                                                          pool_cached, select, select_cached, sweep_layer)
+                                                          Workspace, attend, hsa_chunk, new_frames, plan_sweep,
+                                                          pool, pool_cached, select, select_1d, select_cached,
+                                                          sweep_layer)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
@@ -251,6 +252,7 @@ def main():
     ms_per_step, mean_us, med_us = timed(False)
     ss_ms, ss_mean, ss_med = timed(True)
 
+    one_level = compare_one_level(args, w, g, plan, wss[0], sets[0])
     ceiling = mfma_ceiling()
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
@@ -318,6 +320,7 @@ def main():
         "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in med_us])),
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
         "steady_state": steady,
+        "one_level": one_level,
         "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
@@ -460,6 +463,48 @@ def bench_sweep(args):
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+def compare_one_level(args, w, g, plan, ws, qkv):
+    """HSA against single-level block top-K at the same budget (K = W_b) on one input set:
+    selection time per call, attention time over each list, and the relative L2 distance
+    of each output from dense attention (a fidelity measure on synthetic inputs)."""
+    q, k, v = qkv
+    dev = q.device
+    nb = lf.n_bpf(g)
+    K = plan.W_b
+    lists_1d = torch.empty((w.B, w.H, plan.n_qb, K), dtype=torch.int32, device=dev)
+    n_kb = w.n_kframes * nb
+    full = torch.arange(n_kb, dtype=torch.int32, device=dev).expand(w.B, w.H, plan.n_qb, n_kb).contiguous()
+    hsa_chunk(ws, q, k, v)
+    select_1d(ws, lists_1d)
+    torch.cuda.synchronize()
+
+    def per_call(fn, n=max(5, min(args.steps, 50))):
+        hold_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    o_h, o_1, o_d = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    t_sel_hsa = per_call(lambda: select(ws))
+    t_sel_1d = per_call(lambda: select_1d(ws, lists_1d))
+    t_att_hsa = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, ws.blocks, w.scale, out=o_h))
+    t_att_1d = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, lists_1d, w.scale, out=o_1))
+    lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, full, w.scale, out=o_d)
+    torch.cuda.synchronize()
+    ref = o_d.float()
+    rel = lambda o: float((o.float() - ref).norm() / ref.norm())
+    hb, ob = ws.blocks.cpu().numpy(), lists_1d.cpu().numpy()
+    shared = np.mean([len(np.intersect1d(a, b)) / K for a, b in zip(hb.reshape(-1, K), ob.reshape(-1, K))])
+    return {"K": K, "select_us": {"hsa": round(t_sel_hsa, 2), "one_level": round(t_sel_1d, 2)},
+            "attn_us": {"hsa": round(t_att_hsa, 2), "one_level": round(t_att_1d, 2)},
+            "rel_l2_vs_dense": {"hsa": round(rel(o_h), 5), "one_level": round(rel(o_1), 5)},
+            "shared_block_fraction": round(float(shared), 4)}
 
 
 def compare_schedules(args, s, g, sp_cag, sw_cag, layers, o):

@@ -204,6 +204,23 @@ lf_status lf_select(const float* q_blk, const float* k_frm, const float* k_blk, 
                     int32_t* frames_out, int32_t* blocks_out, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * lf_select_blocks_1d -- the single-granularity selection HSA is contrasted with (Light
+ * Forcing summary, novelty paragraph; 163.com article, ablation section: "1D" sparse
+ * attention): every key block j of the prefix is scored o_r(j) = <q~_r, k~_j>, and the
+ * top K blocks ranked by (score descending, j ascending) form the row's list, ascending.
+ * There is no frame stage and no always-kept frame; for a comparison at equal budget pass
+ * K = the HSA list length W_f*min(k_b, n_bpf).
+ * q_blk: [B, H, n_qb, d] fp32. k_blk: [B, H, n_kframes*n_bpf, d] fp32, (b, h) slices
+ *   g.frame_stride frames apart (0 = packed).
+ * blocks_out: [B, H, n_qb, K] int32, each row ascending; feed it to lf_sparse_attn with
+ *   W_b = K.
+ * Limits: d in {64, 128}; 1 <= K <= n_kframes*n_bpf <= 4096.
+ * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED (d, block count), LF_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_select_blocks_1d(const float* q_blk, const float* k_blk, lf_geom g, int32_t n_qb,
+                              int32_t n_kframes, int32_t K, int32_t* blocks_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * lf_sparse_attn -- [S3], [G2.2] block-sparse attention: each query token t of query
  * block r attends only to the tokens of the blocks listed for r,
  *   o_t = sum_u softmax_u(scale * <q_t, k_u>) v_u   (softmax over the listed tokens).

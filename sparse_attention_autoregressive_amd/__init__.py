@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["Geom", "LfError", "lf_abi_version", "lf_cag_schedule", "lf_block_budget",
-           "lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
+           "lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_select_blocks_1d", "lf_sparse_attn",
            "lf_probe_mfma_bf16", "library_path", "n_bpf"]
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_INFEASIBLE, LF_ERR_HIP = range(5)
@@ -96,6 +96,7 @@ def _load():
         "lf_select_blocks": [vp, vp, Geom, i32, i32, vp, i32, i32, vp, vp],
         "lf_select": [vp, vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, i32, vp, vp, vp],
         "lf_sparse_attn": [vp, vp, vp, vp, i32, Geom, i32, i32, vp, i32, f32, vp],
+        "lf_select_blocks_1d": [vp, vp, Geom, i32, i32, i32, vp, vp],
         "lf_probe_mfma_bf16": [i32, i32, vp, vp, vp],
     }
     for name, args in sig.items():
@@ -296,6 +297,18 @@ def lf_select(q_blk: torch.Tensor, k_frm: torch.Tensor, k_blk: torch.Tensor, g: 
                          None if frames_out is None else _dev(frames_out, "frames_out"),
                          _dev(blocks_out, "blocks_out"), _stream(q_blk)))
     return frames_out, blocks_out
+
+
+def lf_select_blocks_1d(q_blk: torch.Tensor, k_blk: torch.Tensor, g: Geom, n_qb: int, n_kframes: int, K: int,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Single-level block top-K over the whole prefix: ascending lists [B,H,n_qb,K] int32."""
+    lib = _load()
+    if out is None:
+        out = torch.empty((g.B, g.H, n_qb, K), dtype=torch.int32, device=q_blk.device)
+    g = _frame_geom(g, n_kframes, [_pooled(k_blk, "k_blk", g, n_kframes, n_bpf(g))])
+    _check(lib.lf_select_blocks_1d(_dev(q_blk, "q_blk"), k_blk.data_ptr(), g, n_qb, n_kframes, K, _dev(out, "out"),
+                                   _stream(q_blk)))
+    return out
 
 
 def lf_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geom, n_qframes: int,

@@ -305,6 +305,36 @@ lf_status lf_select(const float* q_blk, const float* k_frm, const float* k_blk, 
   return hip_status(lf::launch_select(a, g.d, g.B * g.H * n_qb, true, true, static_cast<hipStream_t>(stream)), fn);
 }
 
+lf_status lf_select_blocks_1d(const float* q_blk, const float* k_blk, lf_geom g, int32_t n_qb,
+                              int32_t n_kframes, int32_t K, int32_t* blocks_out, void* stream) {
+  const char* fn = "lf_select_blocks_1d";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (n_qb < 1 || n_kframes < 1 || K < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_qb, n_kframes and K must be >= 1", fn);
+  const int n_bpf = n_bpf_of(g);
+  const long long n_kb = static_cast<long long>(n_kframes) * n_bpf;
+  if (n_kb > lf::kMax1DBlocks)
+    return fail(LF_ERR_UNSUPPORTED, "%s: %lld key blocks > %d", fn, n_kb, lf::kMax1DBlocks);
+  if (K > n_kb) return fail(LF_ERR_INVALID_ARG, "%s: K=%d > %lld key blocks", fn, K, n_kb);
+  if (!q_blk || !k_blk || !blocks_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q_blk) || !aligned16(k_blk) || (reinterpret_cast<uintptr_t>(blocks_out) & 3u))
+    return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  int fstride = 0;
+  if (lf_status st = pooled_stride(g, n_kframes, &fstride, fn)) return st;
+  const long long rows = static_cast<long long>(g.B) * g.H * n_qb;
+  if (!fits_int(rows) || !fits_int(rows * K) || !fits_int(static_cast<long long>(g.B) * g.H * fstride * n_bpf))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  lf::Select1DArgs a;
+  a.q_blk = q_blk;
+  a.k_blk = k_blk;
+  a.blocks_out = blocks_out;
+  a.n_qb = n_qb;
+  a.n_kb = static_cast<int>(n_kb);
+  a.kb_stride = fstride * n_bpf;
+  a.K = K;
+  pending_error();
+  return hip_status(lf::launch_select_1d(a, g.d, static_cast<int>(rows), static_cast<hipStream_t>(stream)), fn);
+}
+
 lf_status lf_sparse_attn(const void* q, const void* k, const void* v, void* o, lf_dtype dt,
                          lf_geom g, int32_t n_qframes, int32_t n_kframes, const int32_t* blocks,
                          int32_t W_b, float scale, void* stream) {

@@ -62,6 +62,16 @@ struct AttnArgs {
 hipError_t launch_attn_f32(const AttnArgs& a, int d, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnArgs& a, int d, hipStream_t st);
 
+// Single-level block top-k over all n_kb key blocks of a row's prefix.
+constexpr int kMax1DBlocks = 4096;
+struct Select1DArgs {
+  const float* q_blk;   // [rows, D]
+  const float* k_blk;   // (b, h) slices kb_stride blocks apart
+  int* blocks_out;      // [rows, K]
+  int n_qb, n_kb, kb_stride, K;
+};
+hipError_t launch_select_1d(const Select1DArgs& a, int d, int n_rows, hipStream_t st);
+
 // Dense bf16 MFMA loop of n_wg 4-wave workgroups (measurement aid).
 hipError_t launch_mfma_probe(int n_wg, int iters, float* sink, long long* clocks, hipStream_t st);
 

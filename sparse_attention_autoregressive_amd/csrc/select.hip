@@ -188,4 +188,80 @@ hipError_t launch_select(const SelectArgs& a, int d, int n_rows, bool frames, bo
   return launch_select_t<false, true>(a, d, n_rows, st);
 }
 
+// ---------------------------------------------------------------------------------
+// Single-level selection (the one-granularity variant HSA is contrasted with): every key
+// block of the prefix is scored by the same 8-lane group dot product, the rank keys go to
+// LDS, a bitonic sort over the next power of two (empty slots hold key 0, below every
+// real key) orders them, the first K ids are flagged, and wave 0 compacts the flags into
+// the row's ascending list.
+constexpr int kMax1D = 4096;                       // key blocks per row (LDS keys: 32 KB)
+
+template <int D>
+__global__ void __launch_bounds__(kSelThreads) select_1d_kernel(Select1DArgs a) {
+  __shared__ uint64_t key_s[kMax1D];
+  __shared__ unsigned char flag_s[kMax1D];
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int per = nwg / 8, rem = nwg % 8;
+  const int row = xcd * per + min(xcd, rem) + slot;
+  const int bh = row / a.n_qb;
+  const int grp = threadIdx.x / kGroup, c = threadIdx.x % kGroup;
+  const int n = a.n_kb;
+  int np2 = 1;
+  while (np2 < n) np2 <<= 1;
+
+  QSlice<D> q;
+  {
+    const float* qr = a.q_blk + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) q.v[i] = *reinterpret_cast<const float4*>(qr + 4 * c + 32 * i);
+  }
+  const float* kbase = a.k_blk + static_cast<size_t>(bh) * a.kb_stride * D;
+  for (int e = grp; e < n; e += kGroups) {
+    const float sc = group_dot<D>(q, kbase + static_cast<size_t>(e) * D, c);
+    if (c == 0) key_s[e] = rank_key(sc, static_cast<uint32_t>(e));
+  }
+  for (int e = n + threadIdx.x; e < np2; e += kSelThreads) key_s[e] = 0;
+  for (int e = threadIdx.x; e < n; e += kSelThreads) flag_s[e] = 0;
+  __syncthreads();
+  // bitonic sort, descending
+  for (int k = 2; k <= np2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < np2 / 2; i += kSelThreads) {
+        const int lo = 2 * i - (i & (j - 1)), hi = lo + j;
+        const uint64_t x = key_s[lo], y = key_s[hi];
+        const bool desc = (lo & k) == 0;
+        if (desc ? x < y : x > y) {
+          key_s[lo] = y;
+          key_s[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < a.K; i += kSelThreads) flag_s[key_id(key_s[i])] = 1;
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const uint64_t below = lanes_below_mask();
+    int* out = a.blocks_out + static_cast<size_t>(row) * a.K;
+    int count = 0;
+    for (int e0 = 0; e0 < n; e0 += kWave) {
+      const int e = e0 + lane;
+      const bool on = e < n && flag_s[e] != 0;
+      const uint64_t m = __ballot(on);
+      if (on) out[count + __popcll(m & below)] = e;
+      count += __popcll(m);
+    }
+  }
+}
+
+hipError_t launch_select_1d(const Select1DArgs& a, int d, int n_rows, hipStream_t st) {
+  if (d == 128)
+    hipLaunchKernelGGL((select_1d_kernel<128>), dim3(static_cast<unsigned>(n_rows)), dim3(kSelThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((select_1d_kernel<64>), dim3(static_cast<unsigned>(n_rows)), dim3(kSelThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace lf

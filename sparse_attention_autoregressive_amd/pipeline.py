@@ -21,7 +21,7 @@ from typing import List, Sequence
 import torch
 
 from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_pool_qk, lf_select, lf_select_blocks,
-               lf_select_frames, lf_sparse_attn, n_bpf)
+               lf_select_blocks_1d, lf_select_frames, lf_sparse_attn, n_bpf)
 
 
 @dataclass
@@ -103,6 +103,13 @@ def select(ws: Workspace):
     p = ws.plan
     lf_select(ws.q_blk, ws.k_frm, ws.k_blk, p.geom, p.n_qb, p.n_kframes, p.mem, p.forced, p.k_f, p.k_b,
               frames_out=ws.frames, blocks_out=ws.blocks)
+
+
+def select_1d(ws: Workspace, out: torch.Tensor, K: int = 0) -> torch.Tensor:
+    """The single-level comparison selection at the HSA budget (K = W_b unless given):
+    top-K blocks over the whole prefix, written to `out` [B, H, n_qb, K]."""
+    p = ws.plan
+    return lf_select_blocks_1d(ws.q_blk, ws.k_blk, p.geom, p.n_qb, p.n_kframes, K or p.W_b, out=out)
 
 
 def attend(ws: Workspace, q, k, v, out=None):

@@ -254,3 +254,16 @@ def test_probe_validation():
     _err(c.lf_probe_mfma_bf16(4, 0, FAKE, FAKE, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_probe_mfma_bf16(4, 10, FAKE, FAKE + 4, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_probe_mfma_bf16(4, 10, None, FAKE, None), lf.LF_ERR_INVALID_ARG)
+
+
+def test_select_1d_validation():
+    c = _c()
+    F = FAKE
+    g = lf.Geom(1, 2, 128, 1560, 64)                      # 25 blocks per frame
+    _err(c.lf_select_blocks_1d(F, F, g, 75, 21, 0, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_select_blocks_1d(F, F, g, 75, 21, 526, F, None), lf.LF_ERR_INVALID_ARG)     # K > 525 blocks
+    _err(c.lf_select_blocks_1d(F, F, g, 75, 164, 64, F, None), lf.LF_ERR_UNSUPPORTED)    # 4100 blocks
+    _err(c.lf_select_blocks_1d(F, None, g, 75, 21, 64, F, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_select_blocks_1d(F, F, g, 75, 21, 64, F + 2, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_select_blocks_1d(F, F, lf.Geom(1, 2, 128, 1560, 64, 0, 0, 20), 75, 21, 64, F, None),
+         lf.LF_ERR_INVALID_ARG)                                                            # frame stride < 21

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 import sparse_attention_autoregressive_amd as lf
-from support import (compare_attention, compare_masks, lib_k_b, log, oracle_k_b, run_gpu,
+from support import (NEAR_TIE, compare_attention, compare_masks, lib_k_b, log, oracle_k_b, run_gpu,
                      run_oracle_masks, sample_rows)
 
 pytestmark = pytest.mark.gpu
@@ -240,3 +240,34 @@ def test_pool_qk_equals_separate_pools(name):
     torch.cuda.synchronize()
     assert torch.equal(q_blk, q2) and torch.equal(k_blk, k2) and torch.equal(k_frm, f2)
     assert np.array_equal(q2.cpu().numpy(), gpu["q_blk"]) and np.array_equal(f2.cpu().numpy(), gpu["k_frm"])
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_one_level_selection_parity(name):
+    """Single-level block top-K over the whole prefix at the HSA budget (K = W_b): every
+    row's list equals the oracle's (fp64 scores of the oracle's pooling) except where the
+    oracle's cut is a near-tie, lists are ascending, and attention over the GPU's lists
+    matches the oracle's attention over the same lists."""
+    w, x, (q64, k64, v64), gpu, ref, k_b = _case(name)
+    dev = torch.device("cuda")
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    nb = lf.n_bpf(g)
+    n_qb = w.n_qframes * nb
+    K = gpu["blocks"].shape[-1]
+    q_blk, k_blk = (torch.from_numpy(gpu[k]).to(dev) for k in ("q_blk", "k_blk"))
+    got = lf.lf_select_blocks_1d(q_blk, k_blk, g, n_qb, w.n_kframes, K)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want, gaps = oracle.select_blocks_1d(ref["q_blk"], ref["k_blk"], K)
+    rows_g, rows_w = got.reshape(-1, K), want.reshape(-1, K)
+    diff = ~(rows_g == rows_w).all(axis=1)
+    bad = np.nonzero(diff & ~(gaps.reshape(-1) < NEAR_TIE))[0]
+    log(f"[1d] {name}: K={K}, {int(diff.sum())} near-tie rows of {len(rows_g)}")
+    assert len(bad) == 0, (bad[:5], rows_g[bad[0]], rows_w[bad[0]])
+    assert (np.diff(rows_g, axis=1) > 0).all() and rows_g.min() >= 0 and rows_g.max() < w.n_kframes * nb
+    x_dev = [t.to(dev) for t in (x.q, x.k, x.v)]
+    o = lf.lf_sparse_attn(*x_dev, g, w.n_qframes, w.n_kframes, torch.from_numpy(got).to(dev), w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, n_qb, full=(name == "tiny_fp32"))
+    st = compare_attention(w, dict(blocks=got, o=o.float().cpu().numpy()), q64, k64, v64, rows, w.dtype)
+    log(f"[1d] {name}: attention {st}")
