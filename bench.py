@@ -1,13 +1,14 @@
 """Benchmark of the HSA hot path on one MI355X.
 
 One step = one chunk of one layer through the whole path: the CAG schedule and block
-budget on the host, then pooling (query block means, key block and frame means: one
-launch), selection (frame top-k and block top-k: one launch) and block-sparse attention
-on the GPU, each a C-ABI call on torch's current stream.
-Default workload: the 480p layer at chunk 2 of 7 (12 heads x 128, 4680 query tokens
-against 6 frames = 9360 key tokens, 64-token blocks, CAG sparsity s_2 -> 6 frames x 6
-blocks per row); --workload selects the chunk-7 layer, the 69-frame long-memory layer,
-the tiny case or the full 30-layer x 7-chunk CAG sweep.
+budget on the host, then pooling (query block means, key block and frame means),
+selection (frame top-k and block top-k: one launch) and block-sparse attention on the
+GPU, each a C-ABI call on torch's current stream.
+Default workload: the 480p layer at chunk 7 of 7, the headline configuration (12 heads x
+128, 4680 query tokens against 21 frames = 32760 key tokens, 64-token blocks, memory set
+frames 1..17, 4 retrieved frames + sink + the chunk's 3 frames, 8 blocks per frame);
+--workload selects the chunk-2 layer, the 69-frame long-memory layer, the tiny case or
+the full 30-layer x 7-chunk CAG sweep.
 
 Steps cycle over R independent layers' inputs (R chosen so that together they exceed
 twice the 256 MB Infinity Cache), so every step streams its K/V from HBM as in a real
@@ -150,7 +151,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="480p_chunk2of7", choices=sorted(synth.WORKLOADS) + [synth.SWEEP.name])
+    ap.add_argument("--workload", default="480p_chunk7of7", choices=sorted(synth.WORKLOADS) + [synth.SWEEP.name])
     ap.add_argument("--layers", type=int, default=0,
                     help="independent input sets cycled per step (0: enough to exceed 512 MB)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU-oracle sample (0: skip)")

@@ -67,9 +67,17 @@ __device__ __forceinline__ float group_dot(const QSlice<D>& q, const float* __re
 }
 
 // Number of keys among keys[0..n) above `mine` (keys are distinct).
+// Eight keys are read per step, so their LDS reads are in flight together.
 __device__ __forceinline__ int rank_of(uint64_t mine, const uint64_t* keys, int n) {
-  int r = 0;
-  for (int i = 0; i < n; ++i) r += keys[i] > mine ? 1 : 0;
+  int r = 0, i = 0;
+  for (; i + 8 <= n; i += 8) {
+    uint64_t k[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) k[u] = keys[i + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += k[u] > mine ? 1 : 0;
+  }
+  for (; i < n; ++i) r += keys[i] > mine ? 1 : 0;
   return r;
 }
 
