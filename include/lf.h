@@ -149,6 +149,32 @@ lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32
                      int32_t n_kframes, float* q_blk, float* k_blk, float* k_frm, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * lf_qk_prologue -- the query/key prologue before attention (RMSNorm and rotary position
+ * embedding, named among the released deployment kernels in the Light Forcing summary's
+ * reproducibility paragraph and defined nowhere on the pages), fused with [S2] pooling so
+ * the chunk's queries or keys are read from HBM once:
+ *   y = RMSNorm(x) = x / sqrt(mean_c(x_c^2) + eps) * gamma       (over each token's d channels)
+ *   x_out = RoPE(y): adjacent channel pairs (2k, 2k+1) rotate, (a, b) -> (a cos phi - b sin phi,
+ *     a sin phi + b cos phi); of the d/2 pairs the first d/2 - 2*floor(d/6) turn with the
+ *     token's frame (frame0 + frame within x), the next floor(d/6) with its row and the last
+ *     floor(d/6) with its column in the latent frame (tokens_per_frame / lat_w rows of lat_w
+ *     tokens, row-major); pair i of an axis with n pairs has phi = position * theta^(-i/n).
+ *   blk_out, frm_out: the block and frame means of x_out exactly as lf_pool(x_out) would give
+ *     them (bitwise), with g.frame_stride as for lf_pool; frm_out may be NULL.
+ * x, x_out: [B, H, n_frames*tpf, d] in dtype dt, (b, h) slices g.head_stride tokens apart
+ *   (0 = packed); x_out is rounded to dt (round to nearest even) and must not alias x.
+ * gamma: [d] fp32 (device). eps > 0; theta > 1 (10000 in the usual setting).
+ * Numerics: fp32 arithmetic; the rotation uses hardware sine/cosine after reducing
+ *   position * theta^(-i/n) / (2 pi) to [-1/2, 1/2] revolutions (about 1e-6 absolute
+ *   error, far below one bf16 step).
+ * Limits: those of lf_pool; lat_w divides tpf; frame0 >= 0.
+ * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED (d, dtype), LF_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_qk_prologue(const void* x, void* x_out, const float* gamma, lf_dtype dt, lf_geom g,
+                         int32_t n_frames, int32_t frame0, int32_t lat_w, float eps, float theta,
+                         float* blk_out, float* frm_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * lf_select_frames -- [S3] frame stage: for every row (b, h, query block r), the frame
  * relevance p_r(f) = <q~_r, k^_f> over the memory set M; the top-min(k_f, |M|)
  * frames of M ranked by (score descending, frame id ascending) join the always-kept

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["Geom", "LfError", "lf_abi_version", "lf_cag_schedule", "lf_block_budget",
-           "lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_select_blocks_1d", "lf_sparse_attn",
+           "lf_pool", "lf_pool_qk", "lf_qk_prologue", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_select_blocks_1d", "lf_sparse_attn",
            "lf_probe_mfma_bf16", "library_path", "n_bpf"]
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_INFEASIBLE, LF_ERR_HIP = range(5)
@@ -97,6 +97,7 @@ def _load():
         "lf_select": [vp, vp, vp, Geom, i32, i32, pi32, i32, pi32, i32, i32, i32, vp, vp, vp],
         "lf_sparse_attn": [vp, vp, vp, vp, i32, Geom, i32, i32, vp, i32, f32, vp],
         "lf_select_blocks_1d": [vp, vp, Geom, i32, i32, i32, vp, vp],
+        "lf_qk_prologue": [vp, vp, vp, i32, Geom, i32, i32, i32, f32, f32, vp, vp, vp],
         "lf_probe_mfma_bf16": [i32, i32, vp, vp, vp],
     }
     for name, args in sig.items():
@@ -246,6 +247,36 @@ def lf_pool_qk(q: torch.Tensor, k: torch.Tensor, g: Geom, n_qframes: int, n_kfra
     _check(lib.lf_pool_qk(q.data_ptr(), k.data_ptr(), _dtype_code(q), gg, n_qframes, n_kframes,
                           _dev(q_blk, "q_blk"), k_blk.data_ptr(), k_frm.data_ptr(), _stream(q)))
     return q_blk, k_blk, k_frm
+
+
+def lf_qk_prologue(x: torch.Tensor, gamma: torch.Tensor, g: Geom, n_frames: int, frame0: int, lat_w: int,
+                   eps: float = 1e-6, theta: float = 10000.0, x_out: Optional[torch.Tensor] = None,
+                   blk_out: Optional[torch.Tensor] = None, frm_out: Optional[torch.Tensor] = None,
+                   with_frames: bool = True):
+    """RMSNorm + rotary embedding of x into x_out, fused with its block (and frame) means:
+    returns (x_out, blk_out, frm_out or None)."""
+    lib = _load()
+    nb = n_bpf(g)
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if blk_out is None:
+        blk_out = torch.empty((g.B, g.H, n_frames * nb, g.d), dtype=torch.float32, device=x.device)
+    if frm_out is None and with_frames:
+        frm_out = torch.empty((g.B, g.H, n_frames, g.d), dtype=torch.float32, device=x.device)
+    if x_out.dtype != x.dtype:
+        raise TypeError("x_out must have x's dtype")
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (g.d,):
+        raise ValueError(f"gamma must be float32 of shape ({g.d},)")
+    L = n_frames * g.tokens_per_frame
+    sx = _shared("x and x_out", [_tokens(x, "x", g, L), _tokens(x_out, "x_out", g, L)], L)
+    fs = [_pooled(blk_out, "blk_out", g, n_frames, nb)]
+    if frm_out is not None:
+        fs.append(_pooled(frm_out, "frm_out", g, n_frames, 1))
+    gx = _frame_geom(g.with_stride(sx), n_frames, fs)
+    _check(lib.lf_qk_prologue(x.data_ptr(), x_out.data_ptr(), _dev(gamma, "gamma"), _dtype_code(x), gx, n_frames,
+                              frame0, lat_w, float(eps), float(theta), blk_out.data_ptr(),
+                              None if frm_out is None else frm_out.data_ptr(), _stream(x)))
+    return x_out, blk_out, frm_out
 
 
 def lf_select_frames(q_blk: torch.Tensor, k_frm: torch.Tensor, g: Geom, n_qb: int, n_kframes: int,

@@ -258,6 +258,53 @@ lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32
                     fn);
 }
 
+lf_status lf_qk_prologue(const void* x, void* x_out, const float* gamma, lf_dtype dt, lf_geom g, int32_t n_frames,
+                         int32_t frame0, int32_t lat_w, float eps, float theta, float* blk_out, float* frm_out,
+                         void* stream) {
+  const char* fn = "lf_qk_prologue";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (dt != LF_FP32 && dt != LF_BF16) return fail(LF_ERR_UNSUPPORTED, "%s: dtype %d unsupported", fn, (int)dt);
+  if (n_frames < 1 || frame0 < 0) return fail(LF_ERR_INVALID_ARG, "%s: n_frames must be >= 1 and frame0 >= 0", fn);
+  if (lat_w < 1 || g.tokens_per_frame % lat_w != 0)
+    return fail(LF_ERR_INVALID_ARG, "%s: lat_w=%d must divide tokens_per_frame=%d", fn, lat_w, g.tokens_per_frame);
+  if (!(std::isfinite(eps) && eps > 0.f)) return fail(LF_ERR_INVALID_ARG, "%s: eps must be finite and > 0", fn);
+  if (!(std::isfinite(theta) && theta > 1.f)) return fail(LF_ERR_INVALID_ARG, "%s: theta must be finite and > 1", fn);
+  if (!x || !x_out || !gamma || !blk_out) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(x) || !aligned16(x_out) || !aligned16(gamma) || !aligned16(blk_out) || (frm_out && !aligned16(frm_out)))
+    return fail(LF_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  if (x == x_out) return fail(LF_ERR_INVALID_ARG, "%s: x_out must not alias x", fn);
+  const int n_bpf = n_bpf_of(g);
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  const long long len = static_cast<long long>(n_frames) * g.tokens_per_frame;
+  if (!fits_int(BH * n_frames * n_bpf) || !fits_int(BH * n_frames * g.d) || !fits_int(len) ||
+      !fits_int(frame0 + static_cast<long long>(n_frames)))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  if (g.head_stride != 0 && g.head_stride < len)
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < n_frames*tpf = %lld", fn, g.head_stride, len);
+  int out_stride = 0;
+  if (lf_status st = pooled_stride(g, n_frames, &out_stride, fn)) return st;
+  if (!fits_int(BH * out_stride * n_bpf)) return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  lf::ProlArgs a;
+  a.x = x;
+  a.y = x_out;
+  a.gamma = gamma;
+  a.blk = blk_out;
+  a.frm = frm_out;
+  a.stride = g.head_stride ? g.head_stride : len;
+  a.BH = static_cast<int>(BH);
+  a.n_frames = n_frames;
+  a.frame0 = frame0;
+  a.out_stride = out_stride;
+  a.tpf = g.tokens_per_frame;
+  a.bs = g.block_size;
+  a.n_bpf = n_bpf;
+  a.lat_w = lat_w;
+  a.eps = eps;
+  a.theta = theta;
+  pending_error();
+  return hip_status(lf::launch_prologue(a, dt == LF_BF16, g.d, static_cast<hipStream_t>(stream)), fn);
+}
+
 lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
                            int32_t n_kframes, const int32_t* mem, int32_t n_mem,
                            const int32_t* forced, int32_t n_forced, int32_t k_f,

@@ -30,6 +30,19 @@ hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH
 // q_blk, k_frm, lists, n_mem, n_forced, k_eff and writes frames_out (if set). Block
 // stage: reads q_blk, k_blk and the frame lists (from the frame stage, else frames_in)
 // and writes blocks_out.
+// Query/key prologue (RMSNorm + rotary embedding) fused with block (and frame) pooling.
+struct ProlArgs {
+  const void* x;
+  void* y;
+  const float* gamma;   // [d]
+  float* blk;           // block means of y, (b, h) slices out_stride frames apart
+  float* frm;           // frame means, or nullptr
+  long long stride;     // tokens between (b, h) slices of x and y
+  int BH, n_frames, frame0, out_stride, tpf, bs, n_bpf, lat_w;
+  float eps, theta;
+};
+hipError_t launch_prologue(const ProlArgs& a, bool bf16, int d, hipStream_t st);
+
 struct SelectArgs {
   const float* q_blk;
   const float* k_frm;

@@ -202,4 +202,157 @@ hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, in
                          job<float>(x, blk, BH, n_frames, n_bpf, x_stride, out_stride), frm, BH, tpf, bs, n_bpf, st);
 }
 
+// ---------------------------------------------------------------------------------
+// Query/key prologue fused with pooling: RMSNorm over each token's d channels (gamma
+// shared by all heads), then a rotary embedding whose adjacent channel pairs turn with
+// the token's frame, row or column (first d/2 - 2*floor(d/6) pairs, next floor(d/6),
+// last floor(d/6); pair i of an axis with n pairs at position*theta^(-i/n)). The
+// rounded result is stored and, in the same pass, summed into block means exactly as
+// the block-mean kernel would sum the stored tensor (same lanes, batches and order), so
+// a following lf_pool of the output would give bitwise the same means. One wave per
+// block; the 16 lanes of a token (bf16, d = 128) reduce its sum of squares with xor
+// shuffles. Angles are reduced in revolutions and evaluated with the hardware sine and
+// cosine.
+
+template <typename T>
+struct Out16;
+
+template <>
+struct Out16<float> {
+  __device__ static __forceinline__ float round(float x) { return x; }
+  __device__ static __forceinline__ void store(float* p, const float* v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <>
+struct Out16<__bf16> {
+  __device__ static __forceinline__ float round(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
+  __device__ static __forceinline__ void store(__bf16* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+template <typename T>
+struct ProJob {
+  const T* x;
+  T* y;
+  const float* gamma;
+  float* blk;
+  long long stride;      // tokens between (b, h) slices of x and y
+  int n_frames, frame0, out_stride, n_blocks, lat_w;
+  float eps, theta;
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> p, int tpf, int bs, int n_bpf) {
+  constexpr int E = Chunk16<T>::E;
+  constexpr int C = D / E;
+  constexpr int TL = kWave / C;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kPoolWaves + threadIdx.x / kWave);
+  if (w >= p.n_blocks) return;
+  const int lane = threadIdx.x % kWave, c = lane % C, s = lane / C;
+  const int bf = w / n_bpf, j = w - bf * n_bpf;
+  const int bh = bf / p.n_frames, f = bf - bh * p.n_frames;
+  const size_t base = (static_cast<size_t>(bh) * p.stride + static_cast<size_t>(f) * tpf + static_cast<size_t>(j) * bs) * D + c * E;
+  const T* xin = p.x + base;
+  T* yout = p.y + base;
+  const int len = min(bs, tpf - j * bs);
+
+  float gm[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) gm[e] = p.gamma[c * E + e];
+  // the lane's E/2 rotary pairs: axis and turn (revolutions) per unit of position
+  constexpr int NHW = D / 6, NT = D / 2 - 2 * NHW;
+  int axis[E / 2];
+  float rev[E / 2];
+#pragma unroll
+  for (int m = 0; m < E / 2; ++m) {
+    const int k = c * (E / 2) + m;
+    const int ax = k < NT ? 0 : (k < NT + NHW ? 1 : 2);
+    const int i = ax == 0 ? k : (ax == 1 ? k - NT : k - NT - NHW);
+    const int n = ax == 0 ? NT : NHW;
+    axis[m] = ax;
+    rev[m] = static_cast<float>(pow(static_cast<double>(p.theta), -static_cast<double>(i) / n) * 0.15915494309189535);
+  }
+  const int pos_t = p.frame0 + f;
+
+  float a[E], b[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) a[e] = b[e] = 0.f;
+  for (int t0 = 0; t0 < len; t0 += kBatch * TL) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + s + u * TL;
+      v[u] = t < len ? *reinterpret_cast<const uint4*>(xin + static_cast<size_t>(t) * D) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + s + u * TL;
+      float x[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = 0.f;
+      Chunk16<T>::add(reinterpret_cast<const T*>(&v[u]), x);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+      for (int m = 1; m < C; m <<= 1) ss += __shfl_xor(ss, m, kWave);
+      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+      const int tok = j * bs + t;
+      const int pos[3] = {pos_t, tok / p.lat_w, tok % p.lat_w};
+      float o[E];
+#pragma unroll
+      for (int m = 0; m < E / 2; ++m) {
+        const float y0 = x[2 * m] * inv * gm[2 * m], y1 = x[2 * m + 1] * inv * gm[2 * m + 1];
+        float r = static_cast<float>(pos[axis[m]]) * rev[m];
+        r -= rintf(r);
+        const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
+        o[2 * m] = Out16<T>::round(y0 * cs - y1 * sn);
+        o[2 * m + 1] = Out16<T>::round(y0 * sn + y1 * cs);
+      }
+      const bool valid = t < len;
+      if (valid) Out16<T>::store(yout + static_cast<size_t>(t) * D, o);
+#pragma unroll
+      for (int e = 0; e < E; ++e) ((u & 1) ? b : a)[e] += valid ? o[e] : 0.f;
+    }
+  }
+  float sum[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) sum[e] = token_lane_sum<C>(a[e] + b[e]);
+  if (lane < C) {
+    const float invl = 1.0f / static_cast<float>(len);
+    float* out = p.blk + ((static_cast<size_t>(bh) * p.out_stride + f) * n_bpf + j) * D + lane * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4)
+      *reinterpret_cast<float4*>(out + e) =
+          make_float4(sum[e] * invl, sum[e + 1] * invl, sum[e + 2] * invl, sum[e + 3] * invl);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_prologue_t(const ProlArgs& a, hipStream_t st) {
+  ProJob<T> p{static_cast<const T*>(a.x), static_cast<T*>(a.y), a.gamma, a.blk, a.stride, a.n_frames, a.frame0,
+              a.out_stride, a.BH * a.n_frames * a.n_bpf, a.lat_w, a.eps, a.theta};
+  const unsigned grid = static_cast<unsigned>((p.n_blocks + kPoolWaves - 1) / kPoolWaves);
+  hipLaunchKernelGGL((prologue_kernel<T, D>), dim3(grid), dim3(kPoolWaves * kWave), 0, st, p, a.tpf, a.bs, a.n_bpf);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (a.frm == nullptr) return hipSuccess;
+  const int n_sf = a.BH * a.n_frames;
+  const unsigned fgrid = static_cast<unsigned>((static_cast<long long>(n_sf) * D + kFrameThreads - 1) / kFrameThreads);
+  hipLaunchKernelGGL((frame_mean_kernel<D>), dim3(fgrid), dim3(kFrameThreads), 0, st, a.blk, a.frm, n_sf, a.n_frames,
+                     a.out_stride, a.tpf, a.bs, a.n_bpf);
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue(const ProlArgs& a, bool bf16, int d, hipStream_t st) {
+  if (bf16) return d == 128 ? launch_prologue_t<__bf16, 128>(a, st) : launch_prologue_t<__bf16, 64>(a, st);
+  return d == 128 ? launch_prologue_t<float, 128>(a, st) : launch_prologue_t<float, 64>(a, st);
+}
+
 }  // namespace lf

@@ -267,3 +267,24 @@ def test_select_1d_validation():
     _err(c.lf_select_blocks_1d(F, F, g, 75, 21, 64, F + 2, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_select_blocks_1d(F, F, lf.Geom(1, 2, 128, 1560, 64, 0, 0, 20), 75, 21, 64, F, None),
          lf.LF_ERR_INVALID_ARG)                                                            # frame stride < 21
+
+
+def test_prologue_validation():
+    c = _c()
+    F = FAKE
+    g = lf.Geom(1, 2, 128, 1560, 64)
+    call = lambda gg=g, n=3, f0=0, lw=52, eps=1e-6, th=1e4, x=F, y=F + 4096, gm=F: c.lf_qk_prologue(
+        x, y, gm, 1, gg, n, f0, lw, eps, th, F, None, None)
+    _err(call(lw=50), lf.LF_ERR_INVALID_ARG)             # 50 does not divide 1560
+    _err(call(lw=0), lf.LF_ERR_INVALID_ARG)
+    _err(call(eps=0.0), lf.LF_ERR_INVALID_ARG)
+    _err(call(eps=math.nan), lf.LF_ERR_INVALID_ARG)
+    _err(call(th=1.0), lf.LF_ERR_INVALID_ARG)
+    _err(call(f0=-1), lf.LF_ERR_INVALID_ARG)
+    _err(call(n=0), lf.LF_ERR_INVALID_ARG)
+    _err(call(y=F), lf.LF_ERR_INVALID_ARG)               # output aliases input
+    _err(call(gm=None), lf.LF_ERR_INVALID_ARG)
+    _err(call(gm=F + 4), lf.LF_ERR_INVALID_ARG)
+    _err(call(gg=lf.Geom(1, 2, 96, 1560, 64)), lf.LF_ERR_UNSUPPORTED)
+    _err(call(gg=lf.Geom(1, 2, 128, 1560, 64, 4679)), lf.LF_ERR_INVALID_ARG)
+    _err(call(gg=lf.Geom(1, 2, 128, 1560, 64, 0, 0, 2)), lf.LF_ERR_INVALID_ARG)

@@ -271,3 +271,41 @@ def test_one_level_selection_parity(name):
     rows = sample_rows(w, n_qb, full=(name == "tiny_fp32"))
     st = compare_attention(w, dict(blocks=got, o=o.float().cpu().numpy()), q64, k64, v64, rows, w.dtype)
     log(f"[1d] {name}: attention {st}")
+
+
+@pytest.mark.parametrize("name,frame0,lat_w", [("tiny_fp32", 4, 8), ("480p_chunk2of7", 3, 52),
+                                               ("480p_chunk7of7", 18, 52)])
+def test_prologue_parity(name, frame0, lat_w):
+    """RMSNorm + rotary prologue fused with pooling, on the chunk's queries: the output
+    against the oracle (within one step of the stored type, plus fp32 error), and the fused
+    block and frame means equal lf_pool of the output bitwise (and the oracle's pooling of
+    it within the pooling bound)."""
+    from oracle.prologue import qk_prologue
+    w = synth.WORKLOADS[name]
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    rng = np.random.default_rng(77)
+    gamma_np = (1.0 + 0.1 * rng.standard_normal(w.d)).astype(np.float32)
+    gamma = torch.from_numpy(gamma_np).to(dev)
+    q = x.q.to(dev)
+    log(f"[prologue] {name}: frame0 {frame0}, lat_w {lat_w}")
+    y, blk, frm = lf.lf_qk_prologue(q, gamma, g, w.n_qframes, frame0, lat_w)
+    blk2, frm2 = lf.lf_pool(y, g, w.n_qframes)
+    torch.cuda.synchronize()
+    assert torch.equal(blk, blk2) and torch.equal(frm, frm2)
+    q64, _, _ = x.np64()
+    ref = qk_prologue(q64, gamma_np.astype(np.float64), tpf=w.tpf, lat_w=lat_w, frame0=frame0, eps=1e-6)
+    got = y.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    if w.dtype == "bf16":
+        # one bf16 step of the value: the fp32 result (within ~1e-6 of exact) rounds to the
+        # nearest bf16, or to the next one when it lies within that error of a midpoint
+        bound = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7) + 1e-5
+    else:
+        bound = 1e-5 * np.maximum(np.abs(ref), 1.0)
+    log(f"[prologue] {name}: max abs err {err.max():.3e}, worst err/bound {(err / bound).max():.3f}")
+    assert (err <= bound).all()
+    pooled = oracle.pool_blocks(got, w.n_qframes, w.tpf, w.bs)
+    rel = np.abs(blk.cpu().numpy() - pooled).max() / np.abs(pooled).max()
+    assert rel <= 2e-6, rel
