@@ -254,6 +254,7 @@ def main():
     ss_ms, ss_mean, ss_med = timed(True)
 
     one_level = compare_one_level(args, w, g, plan, wss[0], sets[0])
+    prologue = compare_prologue(args, w, g, plan, sets[0])
     ceiling = mfma_ceiling()
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
@@ -322,6 +323,7 @@ def main():
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
         "steady_state": steady,
         "one_level": one_level,
+        "prologue": prologue,
         "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
@@ -466,6 +468,50 @@ def bench_sweep(args):
     print(json.dumps(line))
 
 
+def per_call(fn, n):
+    """Mean device time of one of n back-to-back calls of fn (queued behind a spin kernel)."""
+    hold_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def compare_prologue(args, w, g, plan, qkv):
+    """The query/key prologue (RMSNorm + rotary embedding) fused with pooling, on the
+    chunk's queries and its own key frames (the tensors a step produces before attention
+    in steady state): time per step of the fused calls, their HBM rate, and the time of
+    the separate pooling pass over their outputs that the fusion removes."""
+    q, k, _ = qkv
+    dev = q.device
+    nb = lf.n_bpf(g)
+    f0, tpf, nq = new_frames(plan), w.tpf, w.n_qframes
+    lat_w = 52 if tpf == 1560 else int(round(tpf ** 0.5))
+    kc = k[:, :, f0 * tpf:]
+    gamma = torch.from_numpy((1.0 + 0.1 * np.random.default_rng(77).standard_normal(w.d)).astype(np.float32)).to(dev)
+    qo, ko = torch.empty_like(q), torch.empty((w.B, w.H, nq * tpf, w.d), dtype=q.dtype, device=dev)
+    qb = torch.empty((w.B, w.H, nq * nb, w.d), dtype=torch.float32, device=dev)
+    kb = torch.empty_like(qb)
+    kf = torch.empty((w.B, w.H, nq, w.d), dtype=torch.float32, device=dev)
+
+    def fused():
+        lf.lf_qk_prologue(q, gamma, g, nq, f0, lat_w, x_out=qo, blk_out=qb, with_frames=False)
+        lf.lf_qk_prologue(kc, gamma, g, nq, f0, lat_w, x_out=ko, blk_out=kb, frm_out=kf)
+
+    n = max(5, min(args.steps, 50))
+    t_fused = per_call(fused, n)
+    t_pool = per_call(lambda: lf.lf_pool_qk(qo, ko, g, nq, nq, qb, kb, kf), n)
+    esz = 2 if w.dtype == "bf16" else 4
+    tokens = 2 * w.B * w.H * nq * tpf
+    moved = tokens * w.d * esz * 2 + 2 * w.B * w.H * nq * nb * w.d * 4 + w.B * w.H * nq * w.d * 4
+    return {"what": f"queries and the chunk's own {nq} key frames: RMSNorm + rotary + block/frame means",
+            "lat_w": lat_w, "fused_us": round(t_fused, 2), "hbm_gbs": round(moved / (t_fused * 1e-6) / 1e9, 1),
+            "separate_pool_pass_us": round(t_pool, 2)}
+
+
 def compare_one_level(args, w, g, plan, ws, qkv):
     """HSA against single-level block top-K at the same budget (K = W_b) on one input set:
     selection time per call, attention time over each list, and the relative L2 distance
@@ -481,21 +527,14 @@ def compare_one_level(args, w, g, plan, ws, qkv):
     select_1d(ws, lists_1d)
     torch.cuda.synchronize()
 
-    def per_call(fn, n=max(5, min(args.steps, 50))):
-        hold_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n
-
+    n = max(5, min(args.steps, 50))
     o_h, o_1, o_d = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    t_sel_hsa = per_call(lambda: select(ws))
-    t_sel_1d = per_call(lambda: select_1d(ws, lists_1d))
-    t_att_hsa = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, ws.blocks, w.scale, out=o_h))
-    t_att_1d = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, lists_1d, w.scale, out=o_1))
+    t_sel_hsa = per_call(lambda: select(ws), n)
+    t_sel_1d = per_call(lambda: select_1d(ws, lists_1d), n)
+    t_att_hsa = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, ws.blocks, w.scale,
+                                                   out=o_h), n)
+    t_att_1d = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, lists_1d, w.scale,
+                                                  out=o_1), n)
     lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, full, w.scale, out=o_d)
     torch.cuda.synchronize()
     ref = o_d.float()

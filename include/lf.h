@@ -161,8 +161,10 @@ lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32
  *     tokens, row-major); pair i of an axis with n pairs has phi = position * theta^(-i/n).
  *   blk_out, frm_out: the block and frame means of x_out exactly as lf_pool(x_out) would give
  *     them (bitwise), with g.frame_stride as for lf_pool; frm_out may be NULL.
- * x, x_out: [B, H, n_frames*tpf, d] in dtype dt, (b, h) slices g.head_stride tokens apart
- *   (0 = packed); x_out is rounded to dt (round to nearest even) and must not alias x.
+ * x, x_out: [B, H, n_frames*tpf, d] in dtype dt; the (b, h) slices of x are g.head_stride
+ *   tokens apart and those of x_out g.kv_head_stride apart (each 0 = packed), so a chunk's
+ *   packed projection can be written into a KV cache sized for the clip; x_out is rounded
+ *   to dt (round to nearest even) and must not alias x.
  * gamma: [d] fp32 (device). eps > 0; theta > 1 (10000 in the usual setting).
  * Numerics: fp32 arithmetic; the rotation uses hardware sine/cosine after reducing
  *   position * theta^(-i/n) / (2 pi) to [-1/2, 1/2] revolutions (about 1e-6 absolute

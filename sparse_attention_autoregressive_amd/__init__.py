@@ -253,8 +253,9 @@ def lf_qk_prologue(x: torch.Tensor, gamma: torch.Tensor, g: Geom, n_frames: int,
                    eps: float = 1e-6, theta: float = 10000.0, x_out: Optional[torch.Tensor] = None,
                    blk_out: Optional[torch.Tensor] = None, frm_out: Optional[torch.Tensor] = None,
                    with_frames: bool = True):
-    """RMSNorm + rotary embedding of x into x_out, fused with its block (and frame) means:
-    returns (x_out, blk_out, frm_out or None)."""
+    """RMSNorm + rotary embedding of x into x_out (which may be a token-range view of a
+    KV cache), fused with its block (and frame) means: returns (x_out, blk_out, frm_out or
+    None)."""
     lib = _load()
     nb = n_bpf(g)
     if x_out is None:
@@ -268,11 +269,12 @@ def lf_qk_prologue(x: torch.Tensor, gamma: torch.Tensor, g: Geom, n_frames: int,
     if gamma.dtype != torch.float32 or tuple(gamma.shape) != (g.d,):
         raise ValueError(f"gamma must be float32 of shape ({g.d},)")
     L = n_frames * g.tokens_per_frame
-    sx = _shared("x and x_out", [_tokens(x, "x", g, L), _tokens(x_out, "x_out", g, L)], L)
+    sx = _shared("x", [_tokens(x, "x", g, L)], L)
+    sy = _shared("x_out", [_tokens(x_out, "x_out", g, L)], L)
     fs = [_pooled(blk_out, "blk_out", g, n_frames, nb)]
     if frm_out is not None:
         fs.append(_pooled(frm_out, "frm_out", g, n_frames, 1))
-    gx = _frame_geom(g.with_stride(sx), n_frames, fs)
+    gx = _frame_geom(g.with_stride(sx, sy), n_frames, fs)
     _check(lib.lf_qk_prologue(x.data_ptr(), x_out.data_ptr(), _dev(gamma, "gamma"), _dtype_code(x), gx, n_frames,
                               frame0, lat_w, float(eps), float(theta), blk_out.data_ptr(),
                               None if frm_out is None else frm_out.data_ptr(), _stream(x)))

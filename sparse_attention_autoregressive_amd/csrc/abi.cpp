@@ -281,6 +281,8 @@ lf_status lf_qk_prologue(const void* x, void* x_out, const float* gamma, lf_dtyp
     return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
   if (g.head_stride != 0 && g.head_stride < len)
     return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < n_frames*tpf = %lld", fn, g.head_stride, len);
+  if (g.kv_head_stride != 0 && g.kv_head_stride < len)
+    return fail(LF_ERR_INVALID_ARG, "%s: kv_head_stride %d < n_frames*tpf = %lld", fn, g.kv_head_stride, len);
   int out_stride = 0;
   if (lf_status st = pooled_stride(g, n_frames, &out_stride, fn)) return st;
   if (!fits_int(BH * out_stride * n_bpf)) return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
@@ -290,7 +292,8 @@ lf_status lf_qk_prologue(const void* x, void* x_out, const float* gamma, lf_dtyp
   a.gamma = gamma;
   a.blk = blk_out;
   a.frm = frm_out;
-  a.stride = g.head_stride ? g.head_stride : len;
+  a.x_stride = g.head_stride ? g.head_stride : len;
+  a.y_stride = g.kv_head_stride ? g.kv_head_stride : len;
   a.BH = static_cast<int>(BH);
   a.n_frames = n_frames;
   a.frame0 = frame0;
@@ -300,7 +303,15 @@ lf_status lf_qk_prologue(const void* x, void* x_out, const float* gamma, lf_dtyp
   a.n_bpf = n_bpf;
   a.lat_w = lat_w;
   a.eps = eps;
-  a.theta = theta;
+  // pair k: axis frame for the first d/2 - 2*floor(d/6) pairs, then row, then column;
+  // pair i of an axis with n pairs turns theta^(-i/n) radians per unit of position
+  const int n_hw = g.d / 6, n_t = g.d / 2 - 2 * n_hw;
+  for (int k = 0; k < g.d / 2; ++k) {
+    const int i = k < n_t ? k : (k < n_t + n_hw ? k - n_t : k - n_t - n_hw);
+    const int n = k < n_t ? n_t : n_hw;
+    a.rev[k] = static_cast<float>(std::pow(static_cast<double>(theta), -static_cast<double>(i) / n) /
+                                  (2.0 * 3.14159265358979323846));
+  }
   pending_error();
   return hip_status(lf::launch_prologue(a, dt == LF_BF16, g.d, static_cast<hipStream_t>(stream)), fn);
 }

@@ -31,15 +31,18 @@ hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH
 // stage: reads q_blk, k_blk and the frame lists (from the frame stage, else frames_in)
 // and writes blocks_out.
 // Query/key prologue (RMSNorm + rotary embedding) fused with block (and frame) pooling.
+constexpr int kMaxPairs = 64;   // rotary pairs of the largest head dimension (d = 128)
 struct ProlArgs {
   const void* x;
   void* y;
   const float* gamma;   // [d]
   float* blk;           // block means of y, (b, h) slices out_stride frames apart
   float* frm;           // frame means, or nullptr
-  long long stride;     // tokens between (b, h) slices of x and y
+  long long x_stride;   // tokens between (b, h) slices of x
+  long long y_stride;   // tokens between (b, h) slices of y
   int BH, n_frames, frame0, out_stride, tpf, bs, n_bpf, lat_w;
-  float eps, theta;
+  float eps;
+  float rev[kMaxPairs];   // per rotary pair: theta^(-i/n) / (2 pi), revolutions per unit of position
 };
 hipError_t launch_prologue(const ProlArgs& a, bool bf16, int d, hipStream_t st);
 

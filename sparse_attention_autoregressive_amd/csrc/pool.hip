@@ -210,8 +210,8 @@ hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, in
 // rounded result is stored and, in the same pass, summed into block means exactly as
 // the block-mean kernel would sum the stored tensor (same lanes, batches and order), so
 // a following lf_pool of the output would give bitwise the same means. One wave per
-// block; the 16 lanes of a token (bf16, d = 128) reduce its sum of squares with xor
-// shuffles. Angles are reduced in revolutions and evaluated with the hardware sine and
+// block; the 16 lanes of a token (bf16, d = 128) reduce its sum of squares with DPP
+// lane moves. Angles are reduced in revolutions and evaluated with the hardware sine and
 // cosine.
 
 template <typename T>
@@ -237,15 +237,35 @@ struct Out16<__bf16> {
   }
 };
 
+// Sum over the C consecutive lanes holding one token's chunks, the same value in each:
+// pairs within quads and half-rows and rows with DPP moves (no LDS round trip), wider
+// groups with xor shuffles. Every step adds partners in the same order in both lanes of
+// a pair, so all lanes of the token end with bitwise the same sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int C>
+__device__ __forceinline__ float token_sum(float x) {
+  if (C > 1) x = dpp_add<0xB1>(x);     // quad_perm [1, 0, 3, 2]
+  if (C > 2) x = dpp_add<0x4E>(x);     // quad_perm [2, 3, 0, 1]
+  if (C > 4) x = dpp_add<0x141>(x);    // row_half_mirror
+  if (C > 8) x = dpp_add<0x140>(x);    // row_mirror
+#pragma unroll
+  for (int m = 16; m < C; m <<= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
 template <typename T>
 struct ProJob {
   const T* x;
   T* y;
   const float* gamma;
   float* blk;
-  long long stride;      // tokens between (b, h) slices of x and y
+  long long x_stride, y_stride;   // tokens between (b, h) slices of x and of y
   int n_frames, frame0, out_stride, n_blocks, lat_w;
-  float eps, theta;
+  float eps;
+  float rev[kMaxPairs];           // turn per unit of position of each rotary pair (revolutions)
 };
 
 template <typename T, int D>
@@ -258,9 +278,9 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
   const int lane = threadIdx.x % kWave, c = lane % C, s = lane / C;
   const int bf = w / n_bpf, j = w - bf * n_bpf;
   const int bh = bf / p.n_frames, f = bf - bh * p.n_frames;
-  const size_t base = (static_cast<size_t>(bh) * p.stride + static_cast<size_t>(f) * tpf + static_cast<size_t>(j) * bs) * D + c * E;
-  const T* xin = p.x + base;
-  T* yout = p.y + base;
+  const size_t in_frame = (static_cast<size_t>(f) * tpf + static_cast<size_t>(j) * bs) * D + c * E;
+  const T* xin = p.x + static_cast<size_t>(bh) * p.x_stride * D + in_frame;
+  T* yout = p.y + static_cast<size_t>(bh) * p.y_stride * D + in_frame;
   const int len = min(bs, tpf - j * bs);
 
   float gm[E];
@@ -273,17 +293,19 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
 #pragma unroll
   for (int m = 0; m < E / 2; ++m) {
     const int k = c * (E / 2) + m;
-    const int ax = k < NT ? 0 : (k < NT + NHW ? 1 : 2);
-    const int i = ax == 0 ? k : (ax == 1 ? k - NT : k - NT - NHW);
-    const int n = ax == 0 ? NT : NHW;
-    axis[m] = ax;
-    rev[m] = static_cast<float>(pow(static_cast<double>(p.theta), -static_cast<double>(i) / n) * 0.15915494309189535);
+    axis[m] = k < NT ? 0 : (k < NT + NHW ? 1 : 2);
+    rev[m] = p.rev[k];
   }
   const int pos_t = p.frame0 + f;
+  // the lane's first token of each batch: row and column by one division, then the
+  // column advances by TL per token (wrapping into the next row; a row narrower than TL
+  // wraps several times)
+  const int tok0 = j * bs + s;
 
   float a[E], b[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) a[e] = b[e] = 0.f;
+  int row = 0, col = 0;
   for (int t0 = 0; t0 < len; t0 += kBatch * TL) {
     uint4 v[kBatch];
 #pragma unroll
@@ -294,6 +316,25 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int t = t0 + s + u * TL;
+      if (u == 0) {
+        row = (tok0 + t0) / p.lat_w;
+        col = (tok0 + t0) - row * p.lat_w;
+      } else {
+        col += TL;
+        while (col >= p.lat_w) {
+          col -= p.lat_w;
+          ++row;
+        }
+      }
+      const int pos[3] = {pos_t, row, col};
+      float rc[E / 2], rs[E / 2];
+#pragma unroll
+      for (int m = 0; m < E / 2; ++m) {
+        float r = static_cast<float>(pos[axis[m]]) * rev[m];
+        r -= rintf(r);
+        rc[m] = __builtin_amdgcn_cosf(r);
+        rs[m] = __builtin_amdgcn_sinf(r);
+      }
       float x[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
@@ -301,20 +342,14 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) ss = fmaf(x[e], x[e], ss);
-#pragma unroll
-      for (int m = 1; m < C; m <<= 1) ss += __shfl_xor(ss, m, kWave);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
-      const int tok = j * bs + t;
-      const int pos[3] = {pos_t, tok / p.lat_w, tok % p.lat_w};
+      ss = token_sum<C>(ss);
+      const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
       float o[E];
 #pragma unroll
       for (int m = 0; m < E / 2; ++m) {
         const float y0 = x[2 * m] * inv * gm[2 * m], y1 = x[2 * m + 1] * inv * gm[2 * m + 1];
-        float r = static_cast<float>(pos[axis[m]]) * rev[m];
-        r -= rintf(r);
-        const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
-        o[2 * m] = Out16<T>::round(y0 * cs - y1 * sn);
-        o[2 * m + 1] = Out16<T>::round(y0 * sn + y1 * cs);
+        o[2 * m] = Out16<T>::round(y0 * rc[m] - y1 * rs[m]);
+        o[2 * m + 1] = Out16<T>::round(y0 * rs[m] + y1 * rc[m]);
       }
       const bool valid = t < len;
       if (valid) Out16<T>::store(yout + static_cast<size_t>(t) * D, o);
@@ -337,8 +372,9 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
 
 template <typename T, int D>
 static hipError_t launch_prologue_t(const ProlArgs& a, hipStream_t st) {
-  ProJob<T> p{static_cast<const T*>(a.x), static_cast<T*>(a.y), a.gamma, a.blk, a.stride, a.n_frames, a.frame0,
-              a.out_stride, a.BH * a.n_frames * a.n_bpf, a.lat_w, a.eps, a.theta};
+  ProJob<T> p{static_cast<const T*>(a.x), static_cast<T*>(a.y), a.gamma, a.blk, a.x_stride, a.y_stride, a.n_frames, a.frame0,
+              a.out_stride, a.BH * a.n_frames * a.n_bpf, a.lat_w, a.eps, {}};
+  for (int k = 0; k < D / 2; ++k) p.rev[k] = a.rev[k];
   const unsigned grid = static_cast<unsigned>((p.n_blocks + kPoolWaves - 1) / kPoolWaves);
   hipLaunchKernelGGL((prologue_kernel<T, D>), dim3(grid), dim3(kPoolWaves * kWave), 0, st, p, a.tpf, a.bs, a.n_bpf);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;

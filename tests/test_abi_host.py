@@ -288,3 +288,10 @@ def test_prologue_validation():
     _err(call(gg=lf.Geom(1, 2, 96, 1560, 64)), lf.LF_ERR_UNSUPPORTED)
     _err(call(gg=lf.Geom(1, 2, 128, 1560, 64, 4679)), lf.LF_ERR_INVALID_ARG)
     _err(call(gg=lf.Geom(1, 2, 128, 1560, 64, 0, 0, 2)), lf.LF_ERR_INVALID_ARG)
+
+
+def test_prologue_output_stride_validation():
+    c = _c()
+    F = FAKE
+    _err(c.lf_qk_prologue(F, F + 4096, F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, 4679), 3, 0, 52, 1e-6, 1e4, F, None,
+                          None), lf.LF_ERR_INVALID_ARG)   # output stride below 3 frames

@@ -273,7 +273,7 @@ def test_one_level_selection_parity(name):
     log(f"[1d] {name}: attention {st}")
 
 
-@pytest.mark.parametrize("name,frame0,lat_w", [("tiny_fp32", 4, 8), ("480p_chunk2of7", 3, 52),
+@pytest.mark.parametrize("name,frame0,lat_w", [("tiny_fp32", 4, 8), ("tiny_fp32", 4, 2), ("480p_chunk2of7", 3, 52),
                                                ("480p_chunk7of7", 18, 52)])
 def test_prologue_parity(name, frame0, lat_w):
     """RMSNorm + rotary prologue fused with pooling, on the chunk's queries: the output
@@ -309,3 +309,24 @@ def test_prologue_parity(name, frame0, lat_w):
     pooled = oracle.pool_blocks(got, w.n_qframes, w.tpf, w.bs)
     rel = np.abs(blk.cpu().numpy() - pooled).max() / np.abs(pooled).max()
     assert rel <= 2e-6, rel
+
+
+def test_prologue_into_cache_view_equals_packed():
+    """The prologue reading a token-range view and writing into a token-range view of a
+    larger cache (different head strides on the two sides) gives bitwise the packed
+    results, and writes nothing outside its frames."""
+    w = synth.WORKLOADS["480p_chunk2of7"]
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    gamma = torch.from_numpy((1.0 + 0.1 * np.random.default_rng(5).standard_normal(w.d)).astype(np.float32)).to(dev)
+    k = x.k.to(dev)                                       # 6 frames; prologue of frames 3..5
+    f0, n = 3, 3
+    src = k[:, :, f0 * w.tpf:]
+    y, blk, frm = lf.lf_qk_prologue(src.contiguous(), gamma, g, n, f0, 52)
+    cache = torch.full((w.B, w.H, 10 * w.tpf, w.d), float("nan"), dtype=k.dtype, device=dev)
+    view = cache[:, :, f0 * w.tpf:(f0 + n) * w.tpf]
+    y2, blk2, frm2 = lf.lf_qk_prologue(src, gamma, g, n, f0, 52, x_out=view)
+    torch.cuda.synchronize()
+    assert torch.equal(y, view) and torch.equal(blk, blk2) and torch.equal(frm, frm2)
+    assert torch.isnan(cache[:, :, :f0 * w.tpf]).all() and torch.isnan(cache[:, :, (f0 + n) * w.tpf:]).all()
