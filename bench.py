@@ -156,6 +156,9 @@ def main():
                     help="independent input sets cycled per step (0: enough to exceed 512 MB)")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-min-s", type=float, default=10.0, help="repeat the CPU sample for at least this long")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the comparison legs (single-level selection, prologue, schedules, MFMA ceiling), "
+                         "e.g. so a profiler trace holds only the hot path's dispatches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -253,9 +256,10 @@ def main():
     ms_per_step, mean_us, med_us = timed(False)
     ss_ms, ss_mean, ss_med = timed(True)
 
-    one_level = compare_one_level(args, w, g, plan, wss[0], sets[0])
-    prologue = compare_prologue(args, w, g, plan, sets[0])
-    ceiling = mfma_ceiling()
+    extras = not args.no_extras
+    one_level = compare_one_level(args, w, g, plan, wss[0], sets[0]) if extras else None
+    prologue = compare_prologue(args, w, g, plan, sets[0]) if extras else None
+    ceiling = mfma_ceiling() if extras else None
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
     t_attn = mean_us[2] * 1e-6
@@ -328,7 +332,7 @@ def main():
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_of(w.name)},
-        "mfma_ceiling": {**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]},
+        "mfma_ceiling": ({**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]} if ceiling else None),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
@@ -411,8 +415,8 @@ def bench_sweep(args):
 
     ms_per_step, stage_us, chunk_us = timed(False)
     ss_ms, ss_stage, ss_chunk = timed(True)
-    compare = compare_schedules(args, s, g, sp, sw, layers, o)
-    ceiling = mfma_ceiling()
+    compare = compare_schedules(args, s, g, sp, sw, layers, o) if not args.no_extras else None
+    ceiling = mfma_ceiling() if not args.no_extras else None
     t_attn = stage_us["attn"] * 1e-6
     attn_tflops = f_active / t_attn / 1e12
     cpu = None
@@ -461,7 +465,7 @@ def bench_sweep(args):
         "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_of(s.name)},
-        "mfma_ceiling": {**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]},
+        "mfma_ceiling": ({**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]} if ceiling else None),
         "schedules": compare,
         "cpu_baseline": cpu,
     }
