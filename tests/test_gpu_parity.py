@@ -330,3 +330,24 @@ def test_prologue_into_cache_view_equals_packed():
     torch.cuda.synchronize()
     assert torch.equal(y, view) and torch.equal(blk, blk2) and torch.equal(frm, frm2)
     assert torch.isnan(cache[:, :, :f0 * w.tpf]).all() and torch.isnan(cache[:, :, (f0 + n) * w.tpf:]).all()
+
+
+def test_edge_lists_longer_than_one_segment():
+    # 312 listed blocks per row (13 per frame x 24 frames, every candidate kept): the
+    # attention kernel stages lists 256 blocks at a time, so this walks two segments;
+    # with every block listed the result is dense attention
+    w = _base(tpf=200, bs=16, n_kframes=24, current=(21, 22, 23), sink=(0,), recent=(20,),
+              mem=tuple(range(1, 20)), k_f=19, k_b=13, q_pool=tuple(range(0, 20)), name="two_segments", seed=7010)
+    x, gpu, ref = _edge(w, full=False)
+    assert gpu["blocks"].shape[-1] == 24 * 13
+    q64, k64, v64 = x.np64()
+    dense = oracle.dense_attn(q64, k64, v64, w.scale)
+    assert np.abs(gpu["o"] - dense).max() <= 2e-2
+
+
+def test_edge_maximum_frame_count():
+    # 256 key frames (the selection limit) of one 16-token block each; 252 memory frames
+    # ranked per row
+    w = _base(tpf=16, bs=16, n_kframes=256, current=(253, 254, 255), sink=(0,), recent=(252,),
+              mem=tuple(range(1, 252)), k_f=8, k_b=1, q_pool=tuple(range(0, 252)), name="max_frames", seed=7011)
+    _edge(w)
