@@ -11,10 +11,17 @@
         kernel in the run), so that a counter that over- or under-counts is corrected by
         a transfer of known size. Also records the SHA-256 of the kernel source, so a
         reader (bench.py) can tell whether the figures still describe the current kernel.
+
+    python -m sparse_attention_autoregressive_amd.profsum counters CSV [CSV ...] \
+        --title T --cmd C [--sets S ...]
+        mean per-dispatch value of every counter in the --pmc runs' counter_collection
+        CSV files (one run per counter set), for each library kernel, and the wave-cycle
+        split of the attention kernel; C is the command with <set> for the counter list.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import os
 import re
@@ -99,6 +106,52 @@ def traffic(fetch_db: str, write_db: str, kernel: str, copy_mib: int, workload: 
     return "\n".join(lines)
 
 
+_KERNELS = (("attn_bf16_kernel", "attention"), ("select_kernel", "selection"),
+            ("select_1d_kernel", "single-level selection"), ("block_mean_kernel", "block means"),
+            ("frame_mean_kernel", "frame means"), ("prologue_kernel", "prologue"))
+
+
+def counters(csvs, title: str, cmd: str, asked=None) -> str:
+    vals, sets, durs = {}, [], {}
+    for path in csvs:
+        names = []
+        for r in csv.DictReader(open(path)):
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            for key, label in _KERNELS:
+                if key in r["Kernel_Name"]:
+                    vals.setdefault(label, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+                    if key == "attn_bf16_kernel":
+                        durs[(path, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        sets.append(" ".join(names))
+    cols = [c for s_ in sets for c in s_.split()]
+    out = [f"# {title}", "", "Commands (one run per counter set, from /tmp):", ""]
+    out += [f"- `{cmd.replace('<set>', s_)}`" for s_ in (asked or sets)]
+    out += ["", f"attn.hip sha256: {source_sha()}"]
+    if durs:
+        out.append(f"attention dispatch duration under counters: median {statistics.median(durs.values()):.1f} us")
+    out += ["", "Mean per dispatch (derived counters in rocprofv3's definitions; SQ counters summed over the device):",
+            "", "| kernel | dispatches | " + " | ".join(cols) + " |", "|---|---|" + "---|" * len(cols)]
+    for _, label in _KERNELS:
+        if label not in vals:
+            continue
+        m = vals[label]
+        n = max(len(v) for v in m.values())
+        out.append(f"| {label} | {n} | " + " | ".join(
+            f"{statistics.mean(m[c]):.4g}" if c in m else "-" for c in cols) + " |")
+    a = vals.get("attention", {})
+    if "SQ_WAVE_CYCLES" in a:
+        w = statistics.mean(a["SQ_WAVE_CYCLES"])
+        out += ["", "Attention wave cycles (same units):", ""]
+        for c, what in (("SQ_WAIT_ANY", "waiting on s_waitcnt"), ("SQ_WAIT_INST_ANY", "ready, not issued"),
+                        ("SQ_ACTIVE_INST_ANY", "issuing"), ("SQ_ACTIVE_INST_LDS", "issuing LDS"),
+                        ("SQ_ACTIVE_INST_VMEM", "issuing vector memory"), ("SQ_WAIT_INST_LDS", "waiting on LDS issue")):
+            if c in a:
+                out.append(f"- {what} ({c}): {statistics.mean(a[c]) / w * 100:.1f}%")
+    return "\n".join(out)
+
+
 def read_traffic(path: str):
     """(bytes per dispatch, workload) from a traffic summary if its source hash matches the
     current kernel source, else None."""
@@ -128,9 +181,16 @@ def main(argv=None):
     r.add_argument("--copy-mib", type=int, required=True)
     r.add_argument("--workload", required=True)
     r.add_argument("--cmd", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("csv", nargs="+")
+    k.add_argument("--title", required=True)
+    k.add_argument("--cmd", required=True)
+    k.add_argument("--sets", nargs="*", help="the --pmc lists as given, one per CSV (default: names found)")
     a = ap.parse_args(argv)
     if a.cmd_ == "trace":
         print(trace(a.db, a.title, a.cmd))
+    elif a.cmd_ == "counters":
+        print(counters(a.csv, a.title, a.cmd, a.sets))
     else:
         print(traffic(a.fetch, a.write, a.kernel, a.copy_mib, a.workload, a.cmd))
 
