@@ -127,7 +127,9 @@ def counters(csvs, title: str, cmd: str, asked=None) -> str:
         sets.append(" ".join(names))
     cols = [c for s_ in sets for c in s_.split()]
     out = [f"# {title}", "", "Commands (one run per counter set, from /tmp):", ""]
-    out += [f"- `{cmd.replace('<set>', s_)}`" for s_ in (asked or sets)]
+    for i, found in enumerate(sets):
+        given = asked[i] if asked and i < len(asked) and asked[i] else found
+        out.append(f"- `{cmd.replace('<set>', given)}`")
     out += ["", f"attn.hip sha256: {source_sha()}"]
     if durs:
         out.append(f"attention dispatch duration under counters: median {statistics.median(durs.values()):.1f} us")
