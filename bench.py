@@ -137,6 +137,67 @@ def mfma_ceiling(n_wg: int = 512, iters: int = 20000, reps: int = 3):
             "what": f"register-only v_mfma_f32_32x32x16_bf16 chains, {n_wg} x 4 waves, {iters} x 4 MFMAs per wave"}
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def one_core_baseline(w, k_b: int, min_s: float):
+    """The CPU oracle on one head with BLAS limited to one thread (a single-core figure)."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        tflops, sec, reps, dense = run_cpu_baseline(w, k_b, 1, min_s / 2)
+    return {"value": tflops, "unit": "TFLOP/s", "cores": 1,
+            "sample": f"{w.name}, head 0: pool + select + attention, {reps} repeats in {sec:.1f} s"}
+
+
+def gpu_state_under_load(step, seconds: float = 1.5):
+    """Shader and memory clocks (and socket power where the driver reports it) from
+    rocm-smi, read while steps keep the GPU busy; None if the tool is unavailable."""
+    import re
+    import subprocess
+    import threading
+    res = {}
+
+    def query():
+        for exe in ("/opt/rocm/bin/rocm-smi", "rocm-smi"):
+            try:
+                r = subprocess.run([exe, "-P", "-c", "--json"], capture_output=True, text=True, timeout=20)
+                card = next(iter(json.loads(r.stdout).values()))
+            except Exception:
+                continue
+            for key, val in card.items():
+                num = re.findall(r"[\d.]+", str(val))
+                if not num:
+                    continue
+                kl = key.lower()
+                if "power" in kl and "(w)" in kl:
+                    res["power_w"] = float(num[0])
+                elif "sclk clock speed" in kl:
+                    res["sclk_mhz"] = float(num[0])
+                elif "mclk clock speed" in kl:
+                    res["mclk_mhz"] = float(num[0])
+            return
+
+    t = threading.Thread(target=query)
+    t0 = time.perf_counter()
+    t.start()
+    i = 0
+    while t.is_alive() or time.perf_counter() - t0 < seconds:
+        step(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
+    t.join()
+    torch.cuda.synchronize()
+    return res or None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -251,10 +312,11 @@ def main():
         torch.cuda.synchronize()
         per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(KERNELS))]
                         for i in range(args.steps)]) * 1e3                      # us
-        return wall * 1e3 / args.steps, per.mean(axis=0), np.median(per, axis=0)
+        return wall * 1e3 / args.steps, per.mean(axis=0), np.median(per, axis=0), np.percentile(per, [10, 90], axis=0)
 
-    ms_per_step, mean_us, med_us = timed(False)
-    ss_ms, ss_mean, ss_med = timed(True)
+    ms_per_step, mean_us, med_us, pct_us = timed(False)
+    ss_ms, ss_mean, ss_med, _ = timed(True)
+    state = gpu_state_under_load(lambda i: step(i)) if not args.no_extras else None
 
     extras = not args.no_extras
     one_level = compare_one_level(args, w, g, plan, wss[0], sets[0]) if extras else None
@@ -297,7 +359,8 @@ def main():
                "sample": f"{w.name}, heads 0..{args.cpu_heads - 1} of {w.H}: pool + select + attention "
                          f"in numpy fp64, {reps} repeats ({cpu_dense:.3e} dense-equiv FLOP each) "
                          f"in {cpu_s:.1f} s",
-               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or platform.machine()}
+               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+               "one_core": one_core_baseline(w, k_b, args.cpu_min_s)}
 
     line = {
         "metric": METRIC,
@@ -324,6 +387,8 @@ def main():
         "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
         "kernel_us_mean": dict(zip(KERNELS, [round(float(x), 2) for x in mean_us])),
         "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in med_us])),
+        "kernel_us_p10_p90": {k: [round(float(pct_us[0][i]), 2), round(float(pct_us[1][i]), 2)]
+                              for i, k in enumerate(KERNELS)},
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
         "steady_state": steady,
         "one_level": one_level,
@@ -333,6 +398,7 @@ def main():
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_of(w.name)},
         "mfma_ceiling": ({**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]} if ceiling else None),
+        "gpu_state": state,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
@@ -429,7 +495,7 @@ def bench_sweep(args):
                "sample": f"{w7.name} (chunk 7, layer 0), heads 0..{args.cpu_heads - 1}: pool + select + "
                          f"attention in numpy fp64, {reps} repeats ({cpu_dense:.3e} dense-equiv FLOP each) "
                          f"in {cpu_s:.1f} s",
-               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or platform.machine()}
+               "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
     line = {
         "metric": METRIC,
         "value": f_dense / (ms_per_step * 1e-3) / 1e12,
@@ -518,8 +584,10 @@ def compare_prologue(args, w, g, plan, qkv):
 
 def compare_one_level(args, w, g, plan, ws, qkv):
     """HSA against single-level block top-K at the same budget (K = W_b) on one input set:
-    selection time per call, attention time over each list, and the relative L2 distance
-    of each output from dense attention (a fidelity measure on synthetic inputs)."""
+    selection time per call, attention time over each list and over the full lists
+    (dense attention, the context ratio against sparse), and the relative L2 distance of
+    each output from dense attention (a fidelity measure on synthetic inputs). The calls
+    repeat on one input set, so these are warm (cache-resident) times."""
     q, k, v = qkv
     dev = q.device
     nb = lf.n_bpf(g)
@@ -539,14 +607,16 @@ def compare_one_level(args, w, g, plan, ws, qkv):
                                                    out=o_h), n)
     t_att_1d = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, lists_1d, w.scale,
                                                   out=o_1), n)
-    lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, full, w.scale, out=o_d)
+    t_att_dense = per_call(lambda: lf.lf_sparse_attn(q, k, v, g, w.n_qframes, w.n_kframes, full, w.scale,
+                                                     out=o_d), max(3, n // 5))
     torch.cuda.synchronize()
     ref = o_d.float()
     rel = lambda o: float((o.float() - ref).norm() / ref.norm())
     hb, ob = ws.blocks.cpu().numpy(), lists_1d.cpu().numpy()
     shared = np.mean([len(np.intersect1d(a, b)) / K for a, b in zip(hb.reshape(-1, K), ob.reshape(-1, K))])
     return {"K": K, "select_us": {"hsa": round(t_sel_hsa, 2), "one_level": round(t_sel_1d, 2)},
-            "attn_us": {"hsa": round(t_att_hsa, 2), "one_level": round(t_att_1d, 2)},
+            "attn_us": {"hsa": round(t_att_hsa, 2), "one_level": round(t_att_1d, 2), "dense": round(t_att_dense, 2)},
+            "dense_over_hsa_attn": round(t_att_dense / t_att_hsa, 3),
             "rel_l2_vs_dense": {"hsa": round(rel(o_h), 5), "one_level": round(rel(o_1), 5)},
             "shared_block_fraction": round(float(shared), 4)}
 
