@@ -15,9 +15,15 @@
 //     S^T = K Q^T   (A = K tile from LDS, B = Q fragment kept in registers)
 //     O^T += V^T P^T (A = V^T fragment gathered from LDS, B = P^T straight from the
 //                     S^T accumulator after exp2, no lane shuffles)
-//   The online softmax runs in base 2 with scale*log2(e) folded into the logits; the
-//   running max is shared by the two lanes of a query (one xor-32 shuffle per tile) and
-//   the row sum stays per lane until the end.
+//   The softmax runs in base 2 with scale*log2(e) folded into the logits. Weights are
+//   taken against a per-query reference: the normalised output sum(p v) / sum(p) does not
+//   depend on it, and bf16/fp32 weights keep their relative precision anywhere in their
+//   exponent range, so the reference only has to keep the weights finite. A first pass
+//   fixes it at the query's maximum over the row's first tile and spends no work on a
+//   running maximum. If a later score rose far above it (a row sum beyond 2^40 or not
+//   finite), the workgroup redoes the row with the running maximum (the classic online
+//   softmax: the O accumulator and row sum are rescaled when a tile's maximum exceeds the
+//   one in use by more than a slack). Row sums come from the matrix cores.
 //   Workgroups are numbered head-major and spread so that consecutive rows (same head,
 //   same K/V working set) land on the same XCD and share its L2.
 //
@@ -132,6 +138,9 @@ __device__ __forceinline__ uint2 ds_read_tr16(const lds_u8* p) {
 // Running-max slack (log2 units): the O accumulator and row sum are rescaled only when
 // a tile's maximum exceeds the max in use by more than this, so p = 2^(x - m) <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
+// Fixed-reference pass: a row sum at or beyond this (weights up to ~2^40 above the
+// reference) sends the row to the running-maximum pass, far below fp32 overflow.
+constexpr float kFixedRefLimit = 0x1p40f;
 // Listed blocks staged in LDS at a time (longer lists are walked in segments).
 constexpr int kListSeg = 256;
 
@@ -189,10 +198,12 @@ __device__ __forceinline__ void issue_tile(lds_u8* k_lds, lds_u8* v_lds, rsrc_t 
   }
 }
 
-// One 32-token tile of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// One 32-token tile of one wave: S^T = K Q^T, softmax weights, O^T += V^T P^T. With
+// `track`, the tile's maximum updates the reference (and rescales O and the row sum when
+// it grows past the slack); without, the weights use the reference as it stands.
 template <int D>
 __device__ __forceinline__ void tile_compute(const lds_u8* Kt, const lds_u8* Vt, int nv, int g, float c,
-                                             AttnLane<D>& s) {
+                                             AttnLane<D>& s, bool track) {
   constexpr int KS = AttnLane<D>::KS, DT = AttnLane<D>::DT, ROWB = AttnLane<D>::ROWB;
   typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
   f32x16 sacc;
@@ -227,24 +238,26 @@ __device__ __forceinline__ void tile_compute(const lds_u8* Kt, const lds_u8* Vt,
     for (int v = 0; v < 16; ++v)
       if (8 * (v / 4) + 4 * g + (v % 4) >= nv) sacc[v] = -INFINITY;
   }
-  // scale > 0, so the max of the raw scores gives the max of the scaled ones; lanes j and
-  // j + 32 hold the two key halves of query j
-  float mt = sacc[0];
+  if (track) {
+    // scale > 0, so the max of the raw scores gives the max of the scaled ones; lanes j
+    // and j + 32 hold the two key halves of query j
+    float mt = sacc[0];
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-  mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-  const bool grow = mt > s.m + kRescaleSlack;
-  if (__any(grow)) {
-    const float mn = grow ? mt : s.m;
-    const float corr = fast_exp2(s.m - mn);
-    s.m = mn;
+    for (int v = 1; v < 16; ++v) mt = fmaxf(mt, sacc[v]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+    mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    const bool grow = mt > s.m + kRescaleSlack;
+    if (__any(grow)) {
+      const float mn = grow ? mt : s.m;
+      const float corr = fast_exp2(s.m - mn);
+      s.m = mn;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s.lsum[v] *= corr;
+      for (int v = 0; v < 4; ++v) s.lsum[v] *= corr;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s.acc[dt][v] *= corr;
+        for (int v = 0; v < 16; ++v) s.acc[dt][v] *= corr;
+    }
   }
   // P^T as bf16 pairs; B slot t of pb[ks] is key 16ks + 8(t/4) + 4g + t%4
   uint32_t pw[8];
@@ -358,55 +371,81 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
   };
 
   const int* bl = a.blocks + static_cast<size_t>(work) * a.W_b;
-  for (int seg0 = 0; seg0 < a.W_b; seg0 += kListSeg) {
-    const int nseg = min(kListSeg, a.W_b - seg0);
-    const int nt = 2 * nseg;
-    __syncthreads();                          // previous segment fully consumed
-    for (int i = tid; i < nseg; i += 128) {
-      const int gg = bl[seg0 + i];
-      int2 t0 = make_int2(0, 0), t1 = make_int2(0, 0);
-      if (gg >= 0 && gg < a.n_kb) {
-        const int st = geo.start(gg), len = geo.len(gg);
-        t0 = make_int2(st, min(32, len));
-        if (len > 32) t1 = make_int2(st + 32, len - 32);
-      }
-      tile_s[2 * i] = t0;
-      tile_s[2 * i + 1] = t1;
-    }
-    __syncthreads();
-
-    int t = 0;
-    while (t < nt && tile(t).y == 0) ++t;
-    if (t < nt) {
-      const int2 tt = tile(t);
-      issue_tile<D>(kb0, vb0, kr, vr, tt.x, s, w);
-    }
-    // two tiles per iteration so each LDS buffer index is a compile-time constant
-    while (t < nt) {
-      int t2 = t + 1;
-      while (t2 < nt && tile(t2).y == 0) ++t2;
-      const int nv0 = tile(t).y;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __shared__ int redo_s[2];
+  // pass 0: reference fixed by the first tile; pass 1 (only if a query's row sum left the
+  // safe range): the row again with the running maximum. Unrolled, so each pass's tile
+  // loop is compiled with its own (constant) choice.
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      const bool bad = j < nq && !(s.lsum[0] < kFixedRefLimit);
+      if (l == 0) redo_s[w] = __any(bad) ? 1 : 0;
       __syncthreads();
-      if (t2 < nt) {
-        const int2 tt = tile(t2);
-        issue_tile<D>(kb1, vb1, kr, vr, tt.x, s, w);
-      }
-      if (nq > 0) tile_compute<D>(kb0, vb0, nv0, g, c, s);
-      t = t2;
-      if (t >= nt) break;
-
-      t2 = t + 1;
-      while (t2 < nt && tile(t2).y == 0) ++t2;
-      const int nv1 = tile(t).y;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const bool redo = (redo_s[0] | redo_s[1]) != 0;
       __syncthreads();
-      if (t2 < nt) {
-        const int2 tt = tile(t2);
-        issue_tile<D>(kb0, vb0, kr, vr, tt.x, s, w);
+      if (!redo) break;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s.acc[dt][v] = 0.f;
+      s.m = -1e30f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s.lsum[v] = 0.f;
+    }
+    for (int seg0 = 0; seg0 < a.W_b; seg0 += kListSeg) {
+      const int nseg = min(kListSeg, a.W_b - seg0);
+      const int nt = 2 * nseg;
+      __syncthreads();                          // previous segment fully consumed
+      for (int i = tid; i < nseg; i += 128) {
+        const int gg = bl[seg0 + i];
+        int2 t0 = make_int2(0, 0), t1 = make_int2(0, 0);
+        if (gg >= 0 && gg < a.n_kb) {
+          const int st = geo.start(gg), len = geo.len(gg);
+          t0 = make_int2(st, min(32, len));
+          if (len > 32) t1 = make_int2(st + 32, len - 32);
+        }
+        tile_s[2 * i] = t0;
+        tile_s[2 * i + 1] = t1;
       }
-      if (nq > 0) tile_compute<D>(kb1, vb1, nv1, g, c, s);
-      t = t2;
+      __syncthreads();
+
+      int t = 0;
+      while (t < nt && tile(t).y == 0) ++t;
+      if (t >= nt) continue;
+      issue_tile<D>(kb0, vb0, kr, vr, tile(t).x, s, w);
+      // the segment's first tile (buffer 0) always updates the reference; the loop after it
+      // handles two tiles per iteration (buffers 1, 0) so each LDS buffer index is a
+      // compile-time constant, and tracks the maximum only in the redo pass
+      {
+        int t2 = t + 1;
+        while (t2 < nt && tile(t2).y == 0) ++t2;
+        const int nv0 = tile(t).y;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t2 < nt) issue_tile<D>(kb1, vb1, kr, vr, tile(t2).x, s, w);
+        if (nq > 0) tile_compute<D>(kb0, vb0, nv0, g, c, s, true);
+        t = t2;
+      }
+      while (t < nt) {
+        int t2 = t + 1;
+        while (t2 < nt && tile(t2).y == 0) ++t2;
+        const int nv1 = tile(t).y;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t2 < nt) issue_tile<D>(kb0, vb0, kr, vr, tile(t2).x, s, w);
+        if (nq > 0) tile_compute<D>(kb1, vb1, nv1, g, c, s, pass == 1);
+        t = t2;
+        if (t >= nt) break;
+
+        t2 = t + 1;
+        while (t2 < nt && tile(t2).y == 0) ++t2;
+        const int nv0 = tile(t).y;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t2 < nt) issue_tile<D>(kb1, vb1, kr, vr, tile(t2).x, s, w);
+        if (nq > 0) tile_compute<D>(kb0, vb0, nv0, g, c, s, pass == 1);
+        t = t2;
+      }
     }
   }
 

@@ -176,6 +176,42 @@ def test_edge_skipped_ids():
     assert np.abs(o.float().cpu().numpy() - ref).max() <= 2e-2
 
 
+@pytest.mark.parametrize("hot_key", [8.0, 32.0])
+def test_edge_fixed_reference_redo(hot_key):
+    # The attention kernel first weights a row against each query's maximum over the row's
+    # first tile. Here one listed block scores far above that: queries 0.5 and the block's
+    # keys 8.0 give 0.5 * 8 * 128 / sqrt(128) ~ 45 nats (~65 log2 units, past the fixed-
+    # reference limit of 2^40), keys 32.0 give ~260 log2 units (beyond fp32: the fixed-
+    # reference weights overflow). Either way the row is redone with the running maximum.
+    # Head 0's rows list that block after an ordinary one; head 1's rows do not. Both match
+    # the oracle.
+    w = _base(name=f"redo_{hot_key:g}", seed=7012)
+    x = synth.make(w)
+    dev = torch.device("cuda")
+    g = lf.Geom(w.B, w.H, w.d, w.tpf, w.bs)
+    nb = lf.n_bpf(g)
+    n_qb = 3 * nb
+    hot = 5 * nb + 1                                   # a full 64-token block of frame 5
+    tok0 = 5 * w.tpf + w.bs
+    q = torch.full_like(x.q, 0.5)
+    k = x.k.clone()
+    k[:, :, tok0:tok0 + w.bs] = hot_key
+    lists = np.zeros((1, w.H, n_qb, 3), dtype=np.int32)
+    lists[0, 0] = [0, 3, hot]
+    lists[0, 1] = [1, 2, 7]
+    blk = torch.as_tensor(lists, device=dev)
+    o = lf.lf_sparse_attn(q.to(dev), k.to(dev), x.v.to(dev), g, 3, w.n_kframes, blk, w.scale)
+    q64 = q.double().numpy()
+    k64 = k.double().numpy()
+    v64 = x.v.double().numpy()
+    ref = oracle.sparse_attn(q64, k64, v64, lists, w.tpf, w.bs, w.scale)
+    got = o.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    log(f"[edge] fixed-reference redo (keys {hot_key:g}): max abs err {err:.3e}")
+    assert err <= 2e-2, err
+
+
 def test_edge_constant_values():
     # constant V -> every output equals that constant, up to one bf16 ulp (P is rounded
     # to bf16 for the matrix cores, the normaliser is summed in fp32)
