@@ -20,7 +20,7 @@
 //   depend on it, and bf16/fp32 weights keep their relative precision anywhere in their
 //   exponent range, so the reference only has to keep the weights finite. A first pass
 //   fixes it at the query's maximum over the row's first tile and spends no work on a
-//   running maximum. If a later score rose far above it (a row sum beyond 2^40 or not
+//   running maximum. If a later score rose far above it (a row sum beyond 2^64 or not
 //   finite), the workgroup redoes the row with the running maximum (the classic online
 //   softmax: the O accumulator and row sum are rescaled when a tile's maximum exceeds the
 //   one in use by more than a slack). Row sums come from the matrix cores.
@@ -138,9 +138,10 @@ __device__ __forceinline__ uint2 ds_read_tr16(const lds_u8* p) {
 // Running-max slack (log2 units): the O accumulator and row sum are rescaled only when
 // a tile's maximum exceeds the max in use by more than this, so p = 2^(x - m) <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
-// Fixed-reference pass: a row sum at or beyond this (weights up to ~2^40 above the
-// reference) sends the row to the running-maximum pass, far below fp32 overflow.
-constexpr float kFixedRefLimit = 0x1p40f;
+// Fixed-reference pass: a row sum at or beyond this (weights up to ~2^64 above the
+// reference) sends the row to the running-maximum pass. Below it, with at most 2^18
+// weights per row, O stays finite for any |v| < 2^46.
+constexpr float kFixedRefLimit = 0x1p64f;
 // Listed blocks staged in LDS at a time (longer lists are walked in segments).
 constexpr int kListSeg = 256;
 

@@ -179,12 +179,12 @@ def test_edge_skipped_ids():
 @pytest.mark.parametrize("hot_key", [8.0, 32.0])
 def test_edge_fixed_reference_redo(hot_key):
     # The attention kernel first weights a row against each query's maximum over the row's
-    # first tile. Here one listed block scores far above that: queries 0.5 and the block's
-    # keys 8.0 give 0.5 * 8 * 128 / sqrt(128) ~ 45 nats (~65 log2 units, past the fixed-
-    # reference limit of 2^40), keys 32.0 give ~260 log2 units (beyond fp32: the fixed-
-    # reference weights overflow). Either way the row is redone with the running maximum.
-    # Head 0's rows list that block after an ordinary one; head 1's rows do not. Both match
-    # the oracle.
+    # first tile. Here one listed block scores far above that. Queries 0.5 and the block's
+    # keys 8.0 give 0.5 * 8 * 128 / sqrt(128) ~ 45 nats (~65 log2 units: a row sum near
+    # 2^68, past the fixed-reference limit of 2^64); keys 32.0 give ~260 log2 units (the
+    # fixed-reference weights overflow fp32). Either way the row is redone with the running
+    # maximum. Head 0's rows list that block after an ordinary one; head 1's rows do not.
+    # Both match the oracle.
     w = _base(name=f"redo_{hot_key:g}", seed=7012)
     x = synth.make(w)
     dev = torch.device("cuda")
