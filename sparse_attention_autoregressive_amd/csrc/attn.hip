@@ -410,42 +410,51 @@ __global__ void __launch_bounds__(128, 2) attn_bf16_kernel(AttnArgs a) {
       }
       __syncthreads();
 
-      int t = 0;
-      while (t < nt && tile(t).y == 0) ++t;
+      // next non-empty tile from index i on (nt if none) and its table entry; entries are
+      // read before the barriers that precede their use
+      auto next = [&](int i, int2& e) {
+        e = make_int2(0, 0);
+        for (; i < nt; ++i) {
+          e = tile(i);
+          if (e.y != 0) break;
+        }
+        return i;
+      };
+      int2 cur;
+      int t = next(0, cur);
       if (t >= nt) continue;
-      issue_tile<D>(kb0, vb0, kr, vr, tile(t).x, s, w);
+      issue_tile<D>(kb0, vb0, kr, vr, cur.x, s, w);
       // the segment's first tile (buffer 0) always updates the reference; the loop after it
       // handles two tiles per iteration (buffers 1, 0) so each LDS buffer index is a
       // compile-time constant, and tracks the maximum only in the redo pass
       {
-        int t2 = t + 1;
-        while (t2 < nt && tile(t2).y == 0) ++t2;
-        const int nv0 = tile(t).y;
+        int2 nx;
+        const int t2 = next(t + 1, nx);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t2 < nt) issue_tile<D>(kb1, vb1, kr, vr, tile(t2).x, s, w);
-        if (nq > 0) tile_compute<D>(kb0, vb0, nv0, g, c, s, true);
+        if (t2 < nt) issue_tile<D>(kb1, vb1, kr, vr, nx.x, s, w);
+        if (nq > 0) tile_compute<D>(kb0, vb0, cur.y, g, c, s, true);
         t = t2;
+        cur = nx;
       }
       while (t < nt) {
-        int t2 = t + 1;
-        while (t2 < nt && tile(t2).y == 0) ++t2;
-        const int nv1 = tile(t).y;
+        int2 nx;
+        int t2 = next(t + 1, nx);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t2 < nt) issue_tile<D>(kb0, vb0, kr, vr, tile(t2).x, s, w);
-        if (nq > 0) tile_compute<D>(kb1, vb1, nv1, g, c, s, pass == 1);
+        if (t2 < nt) issue_tile<D>(kb0, vb0, kr, vr, nx.x, s, w);
+        if (nq > 0) tile_compute<D>(kb1, vb1, cur.y, g, c, s, pass == 1);
         t = t2;
+        cur = nx;
         if (t >= nt) break;
 
-        t2 = t + 1;
-        while (t2 < nt && tile(t2).y == 0) ++t2;
-        const int nv0 = tile(t).y;
+        t2 = next(t + 1, nx);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t2 < nt) issue_tile<D>(kb1, vb1, kr, vr, tile(t2).x, s, w);
-        if (nq > 0) tile_compute<D>(kb0, vb0, nv0, g, c, s, pass == 1);
+        if (t2 < nt) issue_tile<D>(kb1, vb1, kr, vr, nx.x, s, w);
+        if (nq > 0) tile_compute<D>(kb0, vb0, cur.y, g, c, s, pass == 1);
         t = t2;
+        cur = nx;
       }
     }
   }
