@@ -187,6 +187,37 @@ def hsa_chunk_cached(ws: Workspace, cache: PooledKeyCache, q: torch.Tensor, k: t
     return ws.o if out is None else out
 
 
+class ChunkGraph:
+    """One chunk's launches (pooling, selection, attention) captured once in a HIP graph
+    and replayed: each replay enqueues the same kernels on the same tensors with one host
+    call, so a host-bound caller (a Python loop submitting ~4 launches per chunk) no
+    longer leaves the GPU idle between them. The captured tensors -- the workspace, the
+    cache, q, k, v and out -- must stay allocated, and new inputs are written into them in
+    place. The library's calls allocate, copy and clear nothing, so every kernel is
+    captured as it runs eagerly and a replay's results equal an eager call's bitwise."""
+
+    def __init__(self, ws: Workspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 cache: "PooledKeyCache | None" = None, out: "torch.Tensor | None" = None):
+        self.ws, self.cache = ws, cache
+        self.tensors = (q, k, v, out)
+        run = (lambda: hsa_chunk_cached(ws, cache, q, k, v, out)) if cache is not None else \
+              (lambda: hsa_chunk(ws, q, k, v, out))
+        side = torch.cuda.Stream(device=q.device)       # default priority
+        side.wait_stream(torch.cuda.current_stream(q.device))
+        with torch.cuda.stream(side):                   # one eager run before capture
+            run()
+        torch.cuda.current_stream(q.device).wait_stream(side)
+        torch.cuda.synchronize(q.device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            run()
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        out = self.tensors[3]
+        return self.ws.o if out is None else out
+
+
 # ------------------------------------------------------------------ Chunk-Aware Growth sweep
 @dataclass
 class SweepPlan:
