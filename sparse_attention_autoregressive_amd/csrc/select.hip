@@ -10,7 +10,8 @@
 // a 64-bit rank key (larger = better; equal scores -> lower id first), in LDS.
 //
 // Frame stage: keys of the memory set M; lane e of wave 0 counts the keys above its own
-// (its rank) and keeps frame e if the rank is below min(k_f, |M|). The kept frames and
+// (its rank) and keeps frame e if the rank is below min(k_f, |M|) (every frame of M, with
+// no scores computed, when k_f >= |M|). The kept frames and
 // the always-kept ones are flagged by frame id and compacted in ascending order into T_r.
 //
 // Block stage: keys of the n_bpf blocks of each frame of T_r (up to kSlots frames per
@@ -117,8 +118,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
 
   int W_f = a.W_f;
   if (FRAMES) {
+    // when the budget covers M every memory frame is kept, and no score is needed
+    const bool keep_all = a.k_eff >= a.n_mem;
     const float* kf = a.k_frm + static_cast<size_t>(bh) * a.kf_stride * D;
-    for (int e = grp; e < a.n_mem; e += kGroups) {
+    for (int e = grp; !keep_all && e < a.n_mem; e += kGroups) {
       const int f = a.lists.mem[e];
       const float s = group_dot<D>(q, kf + static_cast<size_t>(f) * D, c);
       if (c == 0) fkey_s[e] = rank_key(s, static_cast<uint32_t>(f));
@@ -127,7 +130,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
     __syncthreads();
     if (wave == 0) {
       for (int e = lane; e < a.n_mem; e += kWave)
-        if (rank_of(fkey_s[e], fkey_s, a.n_mem) < a.k_eff) flag_s[a.lists.mem[e]] = 1;
+        if (keep_all || rank_of(fkey_s[e], fkey_s, a.n_mem) < a.k_eff) flag_s[a.lists.mem[e]] = 1;
       for (int i = lane; i < a.n_forced; i += kWave) flag_s[a.lists.forced[i]] = 1;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
