@@ -9,10 +9,12 @@
 // (deterministic), and the group's first lane stores the score, packed with its id into
 // a 64-bit rank key (larger = better; equal scores -> lower id first), in LDS.
 //
-// Frame stage: keys of the memory set M; lane e of wave 0 counts the keys above its own
-// (its rank) and keeps frame e if the rank is below min(k_f, |M|) (every frame of M, with
-// no scores computed, when k_f >= |M|). The kept frames and
-// the always-kept ones are flagged by frame id and compacted in ascending order into T_r.
+// Frame stage: keys of the memory set M; thread e counts the keys above its own (its
+// rank) and keeps frame e if the rank is below min(k_f, |M|) (every frame of M, with no
+// scores computed, when k_f >= |M|). The frame ids of M and of the always-kept frames are
+// read with q~ at the start, one per thread, so no list read waits in this chain. The kept
+// frames and the always-kept ones are flagged by frame id and compacted in ascending
+// order into T_r.
 //
 // Block stage: keys of the n_bpf blocks of each frame of T_r (up to kSlots frames per
 // pass); wave w ranks the blocks of slots t = w, w + 4, ... the same way and writes the
@@ -30,6 +32,7 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kGroup = 8;                          // lanes per inner product
 constexpr int kGroups = kSelThreads / kGroup;      // inner products in flight per pass
 constexpr int kSlots = 16;                         // frames of T_r scored per pass
+static_assert(kMaxFrames == kSelThreads, "one frame id per thread");
 
 // x + (x of the lane the DPP control selects), within rows of 16 lanes.
 template <int CTRL>
@@ -116,6 +119,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
     for (int i = 0; i < D / 32; ++i) q.v[i] = *reinterpret_cast<const float4*>(qr + 4 * c + 32 * i);
   }
 
+  // ids of M and of the always-kept frames, one per thread, read with q~ at the start
+  const int mem_id = FRAMES && threadIdx.x < a.n_mem ? a.lists.mem[threadIdx.x] : -1;
+  const int forced_id = FRAMES && threadIdx.x < a.n_forced ? a.lists.forced[threadIdx.x] : -1;
+
   int W_f = a.W_f;
   if (FRAMES) {
     // when the budget covers M every memory frame is kept, and no score is needed
@@ -128,13 +135,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
     }
     for (int i = threadIdx.x; i < a.n_kframes; i += kSelThreads) flag_s[i] = 0;
     __syncthreads();
+    if (mem_id >= 0 && (keep_all || rank_of(fkey_s[threadIdx.x], fkey_s, a.n_mem) < a.k_eff))
+      flag_s[mem_id] = 1;
+    if (forced_id >= 0) flag_s[forced_id] = 1;
+    __syncthreads();
     if (wave == 0) {
-      for (int e = lane; e < a.n_mem; e += kWave)
-        if (keep_all || rank_of(fkey_s[e], fkey_s, a.n_mem) < a.k_eff) flag_s[a.lists.mem[e]] = 1;
-      for (int i = lane; i < a.n_forced; i += kWave) flag_s[a.lists.forced[i]] = 1;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       int count = 0;
       for (int f0 = 0; f0 < a.n_kframes; f0 += kWave) {
         const int f = f0 + lane;
