@@ -17,9 +17,10 @@
 // order into T_r.
 //
 // Block stage: keys of the n_bpf blocks of each frame of T_r (up to kSlots frames per
-// pass); wave w ranks the blocks of slots t = w, w + 4, ... the same way and writes the
-// chosen ids tau*n_bpf + j, ascending in j, to slots t*k_b .. t*k_b + k_b - 1 of the
-// row's list. When k_b covers the frame, every block is listed without scoring.
+// pass); the waves rank the blocks of the pass's frames the same way -- two frames per
+// wave at once, one per half-wave, when n_bpf <= 32 -- and write the chosen ids
+// tau*n_bpf + j, ascending in j, to slots t*k_b .. t*k_b + k_b - 1 of the row's list.
+// When k_b covers the frame, every block is listed without scoring.
 //
 // Rows are dealt head-major to the XCDs, so one head's pooled keys stay in one L2.
 #include "lf_device.h"
@@ -175,11 +176,23 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
       if (c == 0) bkey_s[t][j] = rank_key(s, static_cast<uint32_t>(j));
     }
     __syncthreads();
-    for (int t = wave; t < nt; t += kSelWaves) {
-      const bool mine = lane < n_bpf;
-      const bool on = mine && rank_of(bkey_s[t][lane], bkey_s[t], n_bpf) < kb;
-      const uint64_t m = __ballot(on);
-      if (on) out[(t0 + t) * kb + __popcll(m & below)] = frame_at<FRAMES>(t_s, a, row, W_f, t0 + t) * n_bpf + lane;
+    if (n_bpf <= 32) {
+      // two frames per wave at once: lanes 0-31 rank slot tb, lanes 32-63 slot tb + 1
+      const int half = lane >> 5, jl = lane & 31;
+      const uint64_t below_half = jl == 0 ? 0ull : (~0ull >> (64 - jl)) << (32 * half);
+      for (int tb = 2 * wave; tb < nt; tb += 2 * kSelWaves) {
+        const int t = tb + half;
+        const bool on = t < nt && jl < n_bpf && rank_of(bkey_s[t][jl], bkey_s[t], n_bpf) < kb;
+        const uint64_t m = __ballot(on);
+        if (on) out[(t0 + t) * kb + __popcll(m & below_half)] = frame_at<FRAMES>(t_s, a, row, W_f, t0 + t) * n_bpf + jl;
+      }
+    } else {
+      for (int t = wave; t < nt; t += kSelWaves) {
+        const bool mine = lane < n_bpf;
+        const bool on = mine && rank_of(bkey_s[t][lane], bkey_s[t], n_bpf) < kb;
+        const uint64_t m = __ballot(on);
+        if (on) out[(t0 + t) * kb + __popcll(m & below)] = frame_at<FRAMES>(t_s, a, row, W_f, t0 + t) * n_bpf + lane;
+      }
     }
     __syncthreads();
   }
