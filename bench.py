@@ -22,6 +22,7 @@ selection overhead and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -106,6 +107,57 @@ def traffic_of(workload: str):
     none or it was taken on a different version of the kernel source."""
     got = read_traffic(os.path.join(ROOT, "profiles", f"attn_bf16_{workload}_hbm_traffic.md"))
     return None if got is None else got[0]
+
+
+_HIP = None
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+
+def hip_runtime():
+    """The HIP runtime this process already runs on (the one torch and the library share),
+    for the event flag torch does not expose."""
+    global _HIP
+    if _HIP is None:
+        with open("/proc/self/maps") as f:
+            paths = sorted({line.split()[-1] for line in f if "libamdhip64.so" in line})
+        if len(paths) != 1:
+            raise RuntimeError(f"expected one loaded HIP runtime, found {paths}")
+        hip = ctypes.CDLL(paths[0])
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = hip
+    return _HIP
+
+
+class TimingEvent:
+    """A timing event recorded without the system-scope fence, so recording it writes back
+    and invalidates no cache between the kernels it separates (torch's events do, which
+    makes the kernel after each one start with cold caches). Read only after a device
+    synchronisation."""
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        self._ok(hip_runtime().hipEventCreateWithFlags(ctypes.byref(self.h), HIP_EVENT_DISABLE_SYSTEM_FENCE))
+
+    @staticmethod
+    def _ok(err):
+        if err != 0:
+            raise RuntimeError(f"HIP event call failed with error {err}")
+
+    def record(self, stream):
+        self._ok(hip_runtime().hipEventRecord(self.h, ctypes.c_void_p(stream.cuda_stream)))
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end`."""
+        ms = ctypes.c_float()
+        self._ok(hip_runtime().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h))
+        return ms.value
+
+    def __del__(self):
+        if self.h and _HIP is not None:
+            _HIP.hipEventDestroy(self.h)
 
 
 def hold_stream(ms: float = 50.0):
@@ -305,7 +357,7 @@ def main():
         wall = time.perf_counter() - t0
         # per-call times: the same steps again with events between calls, all enqueued while
         # a spin kernel holds the stream, so host launch gaps do not show up as kernel time
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+        evs = [[TimingEvent() for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
         hold_stream()
         for i in range(args.steps):
             step(i, evs[i], cached=cached)
@@ -445,7 +497,7 @@ def bench_sweep(args):
             mark = None
             if events is not None:
                 def mark(i, stage):
-                    ev = torch.cuda.Event(enable_timing=True)
+                    ev = TimingEvent()
                     ev.record(stream)
                     events.append((i, stage, ev))
             sweep_layer(sw, q, k, v, o, mark, cache=caches[li] if cached else None)
