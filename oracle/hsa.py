@@ -248,7 +248,8 @@ def select_blocks_1d(q_blk: np.ndarray, k_blk: np.ndarray, K: int):
 
 
 def block_mask(blocks: np.ndarray, n_kb: int) -> np.ndarray:
-    """B_r(tau, j) as a dense boolean [B,H,n_qb,n_kb] from the per-row id lists."""
+    """B_r(tau, j) = 1[tau in T_r, j in J_r(tau)] of [S3] as a dense boolean [B,H,n_qb,n_kb]
+    over global block ids tau*n_bpf + j, from the per-row id lists (reading R15)."""
     B, H, n_qb, _ = blocks.shape
     m = np.zeros((B, H, n_qb, n_kb), dtype=bool)
     for b in range(B):
@@ -256,6 +257,20 @@ def block_mask(blocks: np.ndarray, n_kb: int) -> np.ndarray:
             for r in range(n_qb):
                 m[b, h, r, blocks[b, h, r]] = True
     return m
+
+
+def frame_scores(q_blk: np.ndarray, k_frm: np.ndarray, b: int, h: int, r: int,
+                 frames: Sequence[int]) -> np.ndarray:
+    """Frame relevance of [S3], p_r(f) = <q~_r, k^_f>, of row (b, h, r) for each frame in
+    `frames` (raw inner products, reading R10)."""
+    return np.array([float(np.dot(q_blk[b, h, r], k_frm[b, h, int(f)])) for f in frames])
+
+
+def block_scores(q_blk: np.ndarray, k_blk: np.ndarray, b: int, h: int, r: int, tau: int,
+                 n_bpf: int) -> np.ndarray:
+    """Block relevance of [S3], o_r(tau, j) = <q~_r, k~_j^(tau)>, of row (b, h, r) for the
+    blocks j = 0..n_bpf-1 of frame tau."""
+    return np.array([float(np.dot(q_blk[b, h, r], k_blk[b, h, int(tau) * n_bpf + j])) for j in range(n_bpf)])
 
 
 # --------------------------------------------------------------------------- attention

@@ -125,6 +125,20 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _exact(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) -> int:
+    """Checks a packed device tensor of one dtype and one exact shape (id lists, pooled
+    queries); returns its data pointer. Raises ValueError before anything is enqueued."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
 def _tokens(t: torch.Tensor, name: str, g: Geom, n_tokens: int) -> int:
     """Checks a [B, H, n_tokens, d] token tensor whose (b, h) slices are contiguous and
     evenly spaced (a packed tensor, or a token-range view of a bigger one); returns its
@@ -245,7 +259,8 @@ def lf_pool_qk(q: torch.Tensor, k: torch.Tensor, g: Geom, n_qframes: int, n_kfra
     gg = g.with_stride(_shared("q", [_tokens(q, "q", g, lq)], lq), _shared("k", [_tokens(k, "k", g, lk)], lk))
     gg = _frame_geom(gg, n_kframes, [_pooled(k_blk, "k_blk", g, n_kframes, nb), _pooled(k_frm, "k_frm", g, n_kframes, 1)])
     _check(lib.lf_pool_qk(q.data_ptr(), k.data_ptr(), _dtype_code(q), gg, n_qframes, n_kframes,
-                          _dev(q_blk, "q_blk"), k_blk.data_ptr(), k_frm.data_ptr(), _stream(q)))
+                          _exact(q_blk, "q_blk", torch.float32, (g.B, g.H, n_qframes * nb, g.d)),
+                          k_blk.data_ptr(), k_frm.data_ptr(), _stream(q)))
     return q_blk, k_blk, k_frm
 
 
@@ -289,10 +304,12 @@ def lf_select_frames(q_blk: torch.Tensor, k_frm: torch.Tensor, g: Geom, n_qb: in
     W_f = len(forced) + min(k_f, len(mem))
     if out is None:
         out = torch.empty((g.B, g.H, n_qb, max(W_f, 1)), dtype=torch.int32, device=q_blk.device)
+    qp = _exact(q_blk, "q_blk", torch.float32, (g.B, g.H, n_qb, g.d))
+    op = _exact(out, "out", torch.int32, (g.B, g.H, n_qb, max(W_f, 1)))
     g = _frame_geom(g, n_kframes, [_pooled(k_frm, "k_frm", g, n_kframes, 1)])
-    _check(lib.lf_select_frames(_dev(q_blk, "q_blk"), k_frm.data_ptr(), g, n_qb, n_kframes,
+    _check(lib.lf_select_frames(qp, k_frm.data_ptr(), g, n_qb, n_kframes,
                                 _i32_array(mem), len(mem), _i32_array(forced), len(forced), k_f,
-                                _dev(out, "out"), _stream(q_blk)))
+                                op, _stream(q_blk)))
     return out
 
 
@@ -304,9 +321,11 @@ def lf_select_blocks(q_blk: torch.Tensor, k_blk: torch.Tensor, g: Geom, n_qb: in
     W_b = W_f * min(k_b, n_bpf(g))
     if out is None:
         out = torch.empty((g.B, g.H, n_qb, W_b), dtype=torch.int32, device=q_blk.device)
+    qp = _exact(q_blk, "q_blk", torch.float32, (g.B, g.H, n_qb, g.d))
+    fp = _exact(frames, "frames", torch.int32, (g.B, g.H, n_qb, W_f))
+    op = _exact(out, "out", torch.int32, (g.B, g.H, n_qb, W_b))
     g = _frame_geom(g, n_kframes, [_pooled(k_blk, "k_blk", g, n_kframes, n_bpf(g))])
-    _check(lib.lf_select_blocks(_dev(q_blk, "q_blk"), k_blk.data_ptr(), g, n_qb, n_kframes,
-                                _dev(frames, "frames"), W_f, k_b, _dev(out, "out"), _stream(q_blk)))
+    _check(lib.lf_select_blocks(qp, k_blk.data_ptr(), g, n_qb, n_kframes, fp, W_f, k_b, op, _stream(q_blk)))
     return out
 
 
@@ -323,12 +342,14 @@ def lf_select(q_blk: torch.Tensor, k_frm: torch.Tensor, k_blk: torch.Tensor, g: 
         frames_out = torch.empty((g.B, g.H, n_qb, max(W_f, 1)), dtype=torch.int32, device=dev)
     if blocks_out is None:
         blocks_out = torch.empty((g.B, g.H, n_qb, W_b), dtype=torch.int32, device=dev)
+    qp = _exact(q_blk, "q_blk", torch.float32, (g.B, g.H, n_qb, g.d))
+    fp = None if frames_out is None else _exact(frames_out, "frames_out", torch.int32, (g.B, g.H, n_qb, max(W_f, 1)))
+    bp = _exact(blocks_out, "blocks_out", torch.int32, (g.B, g.H, n_qb, W_b))
     g = _frame_geom(g, n_kframes, [_pooled(k_frm, "k_frm", g, n_kframes, 1),
                                    _pooled(k_blk, "k_blk", g, n_kframes, n_bpf(g))])
-    _check(lib.lf_select(_dev(q_blk, "q_blk"), k_frm.data_ptr(), k_blk.data_ptr(), g, n_qb, n_kframes,
+    _check(lib.lf_select(qp, k_frm.data_ptr(), k_blk.data_ptr(), g, n_qb, n_kframes,
                          _i32_array(mem), len(mem), _i32_array(forced), len(forced), k_f, k_b,
-                         None if frames_out is None else _dev(frames_out, "frames_out"),
-                         _dev(blocks_out, "blocks_out"), _stream(q_blk)))
+                         fp, bp, _stream(q_blk)))
     return frames_out, blocks_out
 
 
@@ -338,9 +359,10 @@ def lf_select_blocks_1d(q_blk: torch.Tensor, k_blk: torch.Tensor, g: Geom, n_qb:
     lib = _load()
     if out is None:
         out = torch.empty((g.B, g.H, n_qb, K), dtype=torch.int32, device=q_blk.device)
+    qp = _exact(q_blk, "q_blk", torch.float32, (g.B, g.H, n_qb, g.d))
+    op = _exact(out, "out", torch.int32, (g.B, g.H, n_qb, K))
     g = _frame_geom(g, n_kframes, [_pooled(k_blk, "k_blk", g, n_kframes, n_bpf(g))])
-    _check(lib.lf_select_blocks_1d(_dev(q_blk, "q_blk"), k_blk.data_ptr(), g, n_qb, n_kframes, K, _dev(out, "out"),
-                                   _stream(q_blk)))
+    _check(lib.lf_select_blocks_1d(qp, k_blk.data_ptr(), g, n_qb, n_kframes, K, op, _stream(q_blk)))
     return out
 
 
@@ -356,9 +378,12 @@ def lf_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Geom, n
     lq, lk = n_qframes * g.tokens_per_frame, n_kframes * g.tokens_per_frame
     ga = g.with_stride(_shared("q and out", [_tokens(q, "q", g, lq), _tokens(out, "out", g, lq)], lq),
                        _shared("k and v", [_tokens(k, "k", g, lk), _tokens(v, "v", g, lk)], lk))
+    if not isinstance(blocks, torch.Tensor) or blocks.dim() != 4:
+        raise ValueError("blocks must be a 4-D int32 tensor [B, H, n_qb, W_b]")
+    W_b = blocks.shape[-1]
+    bp = _exact(blocks, "blocks", torch.int32, (g.B, g.H, n_qframes * n_bpf(g), W_b))
     _check(lib.lf_sparse_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              _dtype_code(q), ga, n_qframes, n_kframes, _dev(blocks, "blocks"),
-                              blocks.shape[-1], float(scale), _stream(q)))
+                              _dtype_code(q), ga, n_qframes, n_kframes, bp, W_b, float(scale), _stream(q)))
     return out
 
 

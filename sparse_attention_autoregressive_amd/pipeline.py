@@ -187,35 +187,24 @@ def hsa_chunk_cached(ws: Workspace, cache: PooledKeyCache, q: torch.Tensor, k: t
     return ws.o if out is None else out
 
 
-class ChunkGraph:
-    """One chunk's launches (pooling, selection, attention) captured once in a HIP graph
-    and replayed: each replay enqueues the same kernels on the same tensors with one host
-    call, so a host-bound caller (a Python loop submitting ~4 launches per chunk) no
-    longer leaves the GPU idle between them. The captured tensors -- the workspace, the
-    cache, q, k, v and out -- must stay allocated, and new inputs are written into them in
-    place. The library's calls allocate, copy and clear nothing, so every kernel is
-    captured as it runs eagerly and a replay's results equal an eager call's bitwise."""
-
-    def __init__(self, ws: Workspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                 cache: "PooledKeyCache | None" = None, out: "torch.Tensor | None" = None):
-        self.ws, self.cache = ws, cache
-        self.tensors = (q, k, v, out)
-        run = (lambda: hsa_chunk_cached(ws, cache, q, k, v, out)) if cache is not None else \
-              (lambda: hsa_chunk(ws, q, k, v, out))
-        side = torch.cuda.Stream(device=q.device)       # default priority
-        side.wait_stream(torch.cuda.current_stream(q.device))
-        with torch.cuda.stream(side):                   # one eager run before capture
-            run()
-        torch.cuda.current_stream(q.device).wait_stream(side)
-        torch.cuda.synchronize(q.device)
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
-            run()
-
-    def replay(self) -> torch.Tensor:
-        self.graph.replay()
-        out = self.tensors[3]
-        return self.ws.o if out is None else out
+def denoise_steps(ws: Workspace, cache: PooledKeyCache, k_cache: torch.Tensor, v_cache: torch.Tensor, steps):
+    """The T denoising steps of one chunk in steady state (Light Forcing summary, execution
+    flow: chunk i's sparsity is tied to the T steps it is denoised over, stage 1, and every
+    step selects over the key prefix k_{:i}, stages 2-3). `steps` yields (q, k_chunk,
+    v_chunk, out) per step: the step's queries, the chunk's own keys and values -- copied
+    here into the KV caches at the chunk's frames -- and the output. The history's pooled
+    keys in `cache` are read as they are (pooled once, by the earlier chunks); the chunk's
+    own frames are re-pooled at every step, since their keys change. k_cache and v_cache
+    hold the clip ([B, H, >= n_kframes * tpf, d]); returns the last step's output."""
+    p = ws.plan
+    tpf = p.geom.tokens_per_frame
+    a, b = new_frames(p) * tpf, p.n_kframes * tpf
+    out = None
+    for q, k_new, v_new, out in steps:
+        k_cache[:, :, a:b].copy_(k_new)
+        v_cache[:, :, a:b].copy_(v_new)
+        out = hsa_chunk_cached(ws, cache, q, k_cache[:, :, :b], v_cache[:, :, :b], out)
+    return out
 
 
 # ------------------------------------------------------------------ Chunk-Aware Growth sweep

@@ -99,6 +99,27 @@ def make(w: Workload) -> Inputs:
     return Inputs(_to_dtype(q, w.dtype), _to_dtype(k, w.dtype), _to_dtype(v, w.dtype), pairs, pool)
 
 
+def make_denoise_steps(w: Workload, T: int, step_noise: float = 0.5):
+    """Inputs of the T denoising steps of one chunk: step 0 is `make(w)`; at each later step
+    t the chunk's own frames (the last n_qframes key frames) get new keys and values and
+    the chunk gets new queries -- step 0's tokens plus step_noise * N(0, I), drawn from
+    Generator(PCG64(w.seed + 7919 t)) -- while the history frames' keys and values stay
+    those of step 0. Returns a list of T Inputs."""
+    base = make(w)
+    q0, k0, v0 = (t.to(torch.float32).numpy() for t in (base.q, base.k, base.v))
+    f0 = (w.n_kframes - w.n_qframes) * w.tpf
+    steps = [base]
+    for t in range(1, T):
+        rng = np.random.Generator(np.random.PCG64(w.seed + 7919 * t))
+        k, v = k0.copy(), v0.copy()
+        k[:, :, f0:] += np.float32(step_noise) * rng.standard_normal(k[:, :, f0:].shape, dtype=np.float32)
+        v[:, :, f0:] += np.float32(step_noise) * rng.standard_normal(v[:, :, f0:].shape, dtype=np.float32)
+        q = q0 + np.float32(step_noise) * rng.standard_normal(q0.shape, dtype=np.float32)
+        steps.append(Inputs(_to_dtype(q, w.dtype), _to_dtype(k, w.dtype), _to_dtype(v, w.dtype), base.pairs,
+                            base.planted))
+    return steps
+
+
 def make_sweep_layer(s: Sweep, layer: int) -> Inputs:
     """Q/K/V of all 3*n_chunks frames of one sweep layer (seed s.seed(layer)).
 

@@ -1,45 +1,80 @@
-"""GPU parity of the Chunk-Aware Growth sweep (7 chunks of a 480p clip, one layer at a
-time), run as the sweep driver runs it: token-range views of per-layer Q/K/V/O tensors
-that hold the whole clip. On layers 0 and 29 (CAG schedule) and layer 3 (the uniform
-allocation) every chunk's masks (every row) and outputs (sampled rows; the dense first
-chunk included) are compared with the oracle run on that chunk's slice of the layer."""
+"""GPU parity of the Chunk-Aware Growth sweep (7 chunks of a 480p clip, 30 layers), run as
+the sweep driver runs it: token-range views of per-layer Q/K/V/O tensors that hold the
+whole clip.
+
+Every layer runs twice: uncached (each chunk pools its whole key prefix) and in steady
+state (a per-layer pooled-key cache: each chunk pools only its own key frames). For every
+sparse chunk of every layer both runs' masks are compared with the oracle on every row;
+the steady-state lists, pooled keys and outputs must equal the uncached ones bitwise.
+Attention is compared with the oracle run on the GPU's own lists: every head of layers 0
+and 29, one seeded head (all its rows) of every other layer; the dense first chunk is
+checked to list every block. Layer 3 also runs the uniform allocation CAG is compared
+against."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 import sparse_attention_autoregressive_amd as lf
-from sparse_attention_autoregressive_amd.pipeline import SweepWorkspace, plan_sweep, sweep_layer
-from support import compare_attention, compare_masks, log, oracle_k_b, run_oracle_masks, sample_rows
+from sparse_attention_autoregressive_amd.pipeline import PooledKeyCache, SweepWorkspace, plan_sweep, sweep_layer
+from support import compare_attention, compare_masks, log, oracle_k_b, oracle_masks_from_pools
 
 pytestmark = pytest.mark.gpu
 
+S = synth.SWEEP
 
-@pytest.mark.parametrize("layer,schedule", [(0, "cag"), (29, "cag"), (3, "uniform")])
-def test_sweep_layer_parity(layer, schedule):
-    s = synth.SWEEP
-    g = lf.Geom(s.B, s.H, s.d, s.tpf, s.bs)
-    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5,
-                    schedule=schedule)
-    log(f"[sweep] layer {layer}: generating inputs")
-    x = synth.make_sweep_layer(s, layer)
+
+def _plan(schedule="cag"):
+    g = lf.Geom(S.B, S.H, S.d, S.tpf, S.bs)
+    return g, plan_sweep(g, S.n_chunks, S.frames_per_chunk, S.k_f, S.T, S.s_base, S.s_target, S.d ** -0.5,
+                         schedule=schedule)
+
+
+def _attn_rows(layer, n_qb):
+    if layer in (0, S.n_layers - 1):
+        return [(0, h, r) for h in range(S.H) for r in range(n_qb)]
+    h = int(np.random.default_rng(S.seed(layer)).integers(0, S.H))
+    return [(0, h, r) for r in range(n_qb)]
+
+
+def _check_layer(layer, schedule, cached):
+    g, sp = _plan(schedule)
+    log(f"[sweep] layer {layer} ({schedule}): generating inputs")
+    x = synth.make_sweep_layer(S, layer)
     dev = torch.device("cuda")
     q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
     o = torch.full_like(q, float("nan"))
     sw = SweepWorkspace(sp, q.dtype, dev)
-    log(f"[sweep] layer {layer}: running 7 chunks on the GPU")
+    log(f"[sweep] layer {layer}: 7 chunks on the GPU")
     sweep_layer(sw, q, k, v, o)
+    if cached:
+        o_c = torch.full_like(q, float("nan"))
+        sw_c = SweepWorkspace(sp, q.dtype, dev)
+        cache = PooledKeyCache(g, sp.n_frames, dev)
+        cache.k_blk.fill_(float("nan"))
+        cache.k_frm.fill_(float("nan"))
+        stages = []
+        sweep_layer(sw_c, q, k, v, o_c, mark=lambda i, st: stages.append((i, st)), cache=cache)
     torch.cuda.synchronize()
     assert not torch.isnan(o).any(), "some output token was not written"
+    if cached:
+        assert (1, "pool") in stages and (1, "select") not in stages
+        assert torch.equal(o, o_c), "steady-state outputs differ from the uncached sweep"
+        last = sw.chunks[-1]
+        assert torch.equal(last.k_blk, cache.k_blk) and torch.equal(last.k_frm, cache.k_frm)
     q64, k64, v64 = x.np64()
     o_np = o.float().cpu().numpy()
-    tpf, fpc = s.tpf, s.frames_per_chunk
+    tpf, fpc, nb = S.tpf, S.frames_per_chunk, lf.n_bpf(g)
+    kb_all = oracle.pool_blocks(k64, S.n_frames, tpf, S.bs)       # every frame pooled once
+    kf_all = oracle.pool_frames(k64, S.n_frames, tpf)
     for i, p in enumerate(sp.chunks, 1):
-        w = s.chunk(i, layer, schedule)
+        w = S.chunk(i, layer, schedule)
         assert p.k_b == oracle_k_b(w)
         a, b = (i - 1) * fpc * tpf, i * fpc * tpf
         qi, ki, vi = q64[:, :, a:b], k64[:, :, :b], v64[:, :, :b]
-        ref = run_oracle_masks(w, qi, ki, p.k_b)
+        q_blk = oracle.pool_blocks(qi, fpc, tpf, S.bs)
+        ref = oracle_masks_from_pools(w, q_blk, kb_all[:, :, :i * fpc * nb], kf_all[:, :, :i * fpc], p.k_b)
         if sp.dense(i):
             blocks = sw.full[i].cpu().numpy()
             assert np.array_equal(ref["blocks"], blocks), "dense chunk: oracle lists are not the full lists"
@@ -47,11 +82,26 @@ def test_sweep_layer_parity(layer, schedule):
             ws = sw.chunks[i - 1]
             gpu = dict(frames=ws.frames.cpu().numpy(), blocks=ws.blocks.cpu().numpy())
             stats = compare_masks(gpu, ref, min(p.k_b, p.n_bpf))
+            if cached:
+                wc = sw_c.chunks[i - 1]
+                assert torch.equal(ws.q_blk, wc.q_blk) and torch.equal(ws.frames, wc.frames) \
+                    and torch.equal(ws.blocks, wc.blocks), f"chunk {i}: steady-state lists differ"
+                compare_masks(dict(frames=wc.frames.cpu().numpy(), blocks=wc.blocks.cpu().numpy()), ref,
+                              min(p.k_b, p.n_bpf))
             log(f"[sweep] layer {layer} chunk {i}: masks {stats}")
             blocks = gpu["blocks"]
-        rows = sample_rows(w, p.n_qb, full=False)
+        rows = _attn_rows(layer, p.n_qb)
         st = compare_attention(w, dict(blocks=blocks, o=o_np[:, :, a:b]), qi, ki, vi, rows, "bf16")
         log(f"[sweep] layer {layer} chunk {i} (k_b={p.k_b}, W_b={p.W_b}): attention {st}")
+
+
+@pytest.mark.parametrize("layer", range(S.n_layers))
+def test_sweep_layer_parity(layer):
+    _check_layer(layer, "cag", cached=True)
+
+
+def test_sweep_uniform_allocation_parity():
+    _check_layer(3, "uniform", cached=False)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -84,40 +134,6 @@ def test_token_range_views_equal_packed(dtype):
     assert torch.isnan(big["o"][:, :, :off]).all() and torch.isnan(big["o"][:, :, off + w.lq:]).all()
 
 
-def test_cached_sweep_equals_uncached():
-    """The sweep with a pooled-key cache (each chunk pools only its own key frames, the
-    dense first chunk included, and selects over the cached prefix) gives bitwise the
-    lists and outputs of the uncached sweep, and the cache ends up holding the block and
-    frame means of all 21 frames that chunk 7's uncached pooling computes."""
-    from sparse_attention_autoregressive_amd.pipeline import PooledKeyCache
-    s = synth.SWEEP
-    g = lf.Geom(s.B, s.H, s.d, s.tpf, s.bs)
-    sp = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5)
-    log("[sweep-cache] generating layer 5")
-    x = synth.make_sweep_layer(s, 5)
-    dev = torch.device("cuda")
-    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
-    o_ref, o_c = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
-    sw_ref, sw_c = SweepWorkspace(sp, q.dtype, dev), SweepWorkspace(sp, q.dtype, dev)
-    cache = PooledKeyCache(g, sp.n_frames, dev)
-    cache.k_blk.fill_(float("nan"))
-    cache.k_frm.fill_(float("nan"))
-    stages = []
-    sweep_layer(sw_ref, q, k, v, o_ref)
-    sweep_layer(sw_c, q, k, v, o_c, mark=lambda i, st: stages.append((i, st)), cache=cache)
-    torch.cuda.synchronize()
-    log("[sweep-cache] comparing")
-    assert (1, "pool") in stages and (1, "select") not in stages
-    assert torch.equal(o_ref, o_c)
-    for i in range(2, sp.n_chunks + 1):
-        a, b = sw_ref.chunks[i - 1], sw_c.chunks[i - 1]
-        assert torch.equal(a.q_blk, b.q_blk), i
-        assert torch.equal(a.frames, b.frames), i
-        assert torch.equal(a.blocks, b.blocks), i
-    last = sw_ref.chunks[-1]
-    assert torch.equal(last.k_blk, cache.k_blk) and torch.equal(last.k_frm, cache.k_frm)
-
-
 @pytest.mark.parametrize("name", ["tiny_fp32", "480p_chunk2of7"])
 def test_steady_state_chunk_equals_uncached(name):
     """One chunk in steady state: packed queries and output, keys and values a prefix of a
@@ -125,8 +141,7 @@ def test_steady_state_chunk_equals_uncached(name):
     differ), the history's pooled keys in a cache filled beforehand. Pooled queries, the
     cache's new frames, lists and output equal the uncached call on packed tensors
     bitwise."""
-    from sparse_attention_autoregressive_amd.pipeline import (PooledKeyCache, Workspace, hsa_chunk,
-                                                              hsa_chunk_cached, new_frames)
+    from sparse_attention_autoregressive_amd.pipeline import Workspace, hsa_chunk, hsa_chunk_cached, new_frames
     from support import lib_k_b, plan_of
     w = synth.WORKLOADS[name]
     x = synth.make(w)

@@ -50,6 +50,16 @@ def test_hand_worked_example():
     assert out["frames"][0, 0].tolist() == np.array(g["frames"], int).reshape(n_q, -1).tolist()
     assert out["blocks"][0, 0].tolist() == np.array(g["blocks"], int).reshape(n_q, -1).tolist()
     assert np.allclose(out["k_frm"][0, 0], np.array(g["frame_means"]).reshape(-1, d), atol=0)
+    # p_r over M = {1, 2}, o_r over each frame of T_r, and the dense mask B_r
+    mem = [int(x) for x in g["mem"]]
+    for r in range(n_q):
+        assert oracle.frame_scores(out["q_blk"], out["k_frm"], 0, 0, r, mem).tolist() == g[f"frame_scores_r{r}"]
+        got = [oracle.block_scores(out["q_blk"], out["k_blk"], 0, 0, r, tau, out["n_bpf"]).tolist()
+               for tau in out["frames"][0, 0, r]]
+        assert sum(got, []) == g[f"block_scores_r{r}"]
+    n_kb = int(g["n_kframes"][0]) * out["n_bpf"]
+    mask = oracle.block_mask(out["blocks"], n_kb)
+    assert mask[0, 0].astype(int).reshape(-1).tolist() == [int(x) for x in g["mask"]]
     e1, e2 = math.exp(c), math.exp(2 * c)
     den = 2 * e1 + e2
     assert out["o"][0, 0, 0].tolist() == pytest.approx([(2 * e2 + 6 * e1) / den, 1.0], abs=1e-14)
@@ -232,16 +242,34 @@ def test_sparse_equals_library_masked_sdpa():
     q, k, v = x.np64()
     out = oracle.hsa(q, k, v, tpf=w.tpf, bs=w.bs, n_kframes=w.n_kframes, mem=w.mem,
                      forced=w.forced, k_f=w.k_f, k_b=w.k_b, scale=w.scale)
+    n_kb = w.n_kframes * out["n_bpf"]
+    bmask = oracle.block_mask(out["blocks"], n_kb)
     tok_mask = np.zeros((1, w.H, w.lq, w.lk), dtype=bool)
     for h in range(w.H):
         for r in range(out["blocks"].shape[2]):
             qt = oracle.block_tokens(r, w.tpf, w.bs)
-            for g in out["blocks"][0, h, r]:
-                kt = oracle.block_tokens(int(g), w.tpf, w.bs)
-                tok_mask[0, h, qt[:, None], kt[None, :]] = True
+            for g in range(n_kb):
+                if bmask[0, h, r, g]:
+                    kt = oracle.block_tokens(g, w.tpf, w.bs)
+                    tok_mask[0, h, qt[:, None], kt[None, :]] = True
     assert tok_mask.sum() < tok_mask.size                              # really sparse
     ref = _sdpa64(q, k, v, mask=tok_mask, scale=w.scale)
     assert np.abs(out["o"] - ref).max() < 1e-12
+
+
+def test_block_mask_round_trip():
+    """B_r as a dense mask holds exactly the listed ids: per row, its set positions are the
+    row's (ascending, unique) list and its count is the list width."""
+    rng = np.random.default_rng(9)
+    n_kb, W = 40, 7
+    lists = np.sort(np.stack([rng.choice(n_kb, W, replace=False) for _ in range(2 * 3 * 5)]), axis=1)
+    blocks = lists.reshape(2, 3, 5, W)
+    m = oracle.block_mask(blocks, n_kb)
+    assert m.shape == (2, 3, 5, n_kb) and (m.sum(axis=-1) == W).all()
+    for b in range(2):
+        for h in range(3):
+            for r in range(5):
+                assert np.nonzero(m[b, h, r])[0].tolist() == blocks[b, h, r].tolist()
 
 
 def test_attention_closed_forms():
