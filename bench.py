@@ -80,6 +80,13 @@ def pool_bytes(w, n_frames, with_frames):
     return rd + wr
 
 
+def lag_bytes(w, n_lag):
+    """Algorithmic HBM bytes of the lagged frame means of a steady-state pooling launch:
+    read the frames' cached block means, write one mean per frame."""
+    nb = -(-w.tpf // w.bs)
+    return w.B * w.H * n_lag * (nb + 1) * w.d * 4
+
+
 def run_cpu_baseline(w, k_b: int, heads: int, min_s: float):
     """The CPU oracle (numpy fp64) on the first `heads` heads of one layer: pool, select
     and attend, repeated until at least `min_s` seconds have passed. Returns
@@ -187,6 +194,27 @@ def mfma_ceiling(n_wg: int = 512, iters: int = 20000, reps: int = 3):
             best = (tf, ghz)
     return {"tflops": round(best[0], 1), "clock_ghz": round(best[1], 3),
             "what": f"register-only v_mfma_f32_32x32x16_bf16 chains, {n_wg} x 4 waves, {iters} x 4 MFMAs per wave"}
+
+
+def hbm_ceiling(gib: int = 2, reps: int = 5):
+    """Measured HBM read rate: a plain streaming read of a `gib` GiB buffer (8x the 256 MB
+    Infinity Cache, so it streams from HBM), best of `reps` launches."""
+    dev = torch.device("cuda")
+    x = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
+    n_wg = 256 * 8
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lf.lf_probe_hbm_read(x, n_wg, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return {"gbs": round(best, 1), "what": f"plain streaming read of {gib} GiB, {n_wg} x 256 threads, "
+                                           f"16-byte loads, best of {reps}"}
 
 
 def cpu_model() -> str:
@@ -322,6 +350,7 @@ def main():
     # steady state: the history frames' pooled keys sit in a per-layer cache (filled here,
     # before timing); a step pools the queries and the chunk's own key frames only
     f0 = new_frames(plan)
+    n_lag = min(w.n_qframes, f0)
     caches = [PooledKeyCache(g, w.n_kframes, dev) for _ in sets]
     for c, (_, k, _) in zip(caches, sets):
         lf.lf_pool(k[:, :, :f0 * w.tpf], g, f0, blk_out=c.blk(0, f0), frm_out=c.frm(0, f0))
@@ -374,6 +403,7 @@ def main():
     one_level = compare_one_level(args, w, g, plan, wss[0], sets[0]) if extras else None
     prologue = compare_prologue(args, w, g, plan, sets[0]) if extras else None
     ceiling = mfma_ceiling() if extras else None
+    hbm = hbm_ceiling() if extras else None
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
     t_attn = mean_us[2] * 1e-6
@@ -391,16 +421,16 @@ def main():
     sel_gbs = {"select": sel_bytes / (mean_us[1] * 1e-6) / 1e9}
     steady = {
         "what": (f"history pooled keys ({f0} frames) from a per-layer cache filled before timing; a step pools "
-                 f"the queries and the chunk's own {w.n_kframes - f0} key frames, selects over the cache "
-                 f"and attends"),
+                 f"the queries and the chunk's own {w.n_kframes - f0} key frames (block means) with the "
+                 f"previous chunk's {n_lag} frame means in one launch, selects over the cache and attends"),
         "value": f_dense / (ss_ms * 1e-3) / 1e12,
         "ms_per_step": ss_ms,
         "kernel_us_mean": dict(zip(KERNELS, [round(float(x), 2) for x in ss_mean])),
         "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in ss_med])),
         "pool_select_pct_of_attn": 100.0 * ss_mean[:2].sum() / ss_mean[2],
         "dense_equiv_tflops_kernel_sum": f_dense / (ss_mean.sum() * 1e-6) / 1e12,
-        "pool_gbs": round((pool_bytes(w, w.n_qframes, False) + pool_bytes(w, w.n_kframes - f0, True))
-                          / (ss_mean[0] * 1e-6) / 1e9, 1),
+        "pool_gbs": round((pool_bytes(w, w.n_qframes, False) + pool_bytes(w, w.n_kframes - f0, False)
+                           + lag_bytes(w, n_lag)) / (ss_mean[0] * 1e-6) / 1e9, 1),
     }
 
     cpu = None
@@ -442,6 +472,10 @@ def main():
         "kernel_us_p10_p90": {k: [round(float(pct_us[0][i]), 2), round(float(pct_us[1][i]), 2)]
                               for i, k in enumerate(KERNELS)},
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
+        "hbm_ceiling": ({**hbm, "pool_frac": round(pool_gbs["pool"] / hbm["gbs"], 3),
+                         "steady_pool_frac": round(steady["pool_gbs"] / hbm["gbs"], 3),
+                         "prologue_frac": (round(prologue["hbm_gbs"] / hbm["gbs"], 3) if prologue else None)}
+                        if hbm else None),
         "steady_state": steady,
         "one_level": one_level,
         "prologue": prologue,
@@ -500,7 +534,8 @@ def bench_sweep(args):
                     ev = TimingEvent()
                     ev.record(stream)
                     events.append((i, stage, ev))
-            sweep_layer(sw, q, k, v, o, mark, cache=caches[li] if cached else None)
+            # the last chunk's frame means are read by no chunk of the sweep: not formed
+            sweep_layer(sw, q, k, v, o, mark, cache=caches[li] if cached else None, complete=False)
 
     def timed(cached):
         """(ms per sweep by wall clock, per-stage us, per-chunk us of one evented sweep)."""
@@ -605,32 +640,46 @@ def per_call(fn, n):
 def compare_prologue(args, w, g, plan, qkv):
     """The query/key prologue (RMSNorm + rotary embedding) fused with pooling, on the
     chunk's queries and its own key frames (the tensors a step produces before attention
-    in steady state): time per step of the fused calls, their HBM rate, and the time of
-    the separate pooling pass over their outputs that the fusion removes."""
+    in steady state): one launch (lf_qk_prologue_step: queries, keys into a KV cache view,
+    block means, the previous chunk's frame means), its HBM rate, the two-call form it
+    replaces (one lf_qk_prologue per tensor) and the separate pooling pass over their
+    outputs that the fusion removes."""
     q, k, _ = qkv
     dev = q.device
     nb = lf.n_bpf(g)
     f0, tpf, nq = new_frames(plan), w.tpf, w.n_qframes
+    n_lag = min(nq, f0)
     lat_w = 52 if tpf == 1560 else int(round(tpf ** 0.5))
-    kc = k[:, :, f0 * tpf:]
+    kc = k[:, :, f0 * tpf:].contiguous()                  # the chunk's new keys, packed as projected
     gamma = torch.from_numpy((1.0 + 0.1 * np.random.default_rng(77).standard_normal(w.d)).astype(np.float32)).to(dev)
     qo, ko = torch.empty_like(q), torch.empty((w.B, w.H, nq * tpf, w.d), dtype=q.dtype, device=dev)
     qb = torch.empty((w.B, w.H, nq * nb, w.d), dtype=torch.float32, device=dev)
     kb = torch.empty_like(qb)
     kf = torch.empty((w.B, w.H, nq, w.d), dtype=torch.float32, device=dev)
+    cache = PooledKeyCache(g, w.n_kframes, dev)
+    lf.lf_pool(k[:, :, :f0 * tpf], g, f0, blk_out=cache.blk(0, f0), frm_out=cache.frm(0, f0))
 
-    def fused():
+    def one_launch():
+        lf.lf_qk_prologue_step(q, kc, gamma, gamma, g, nq, f0, lat_w, f0, f0 - n_lag, n_lag, ko, cache.k_blk,
+                               cache.k_frm, q_out=qo, q_blk=qb)
+
+    def two_calls():
         lf.lf_qk_prologue(q, gamma, g, nq, f0, lat_w, x_out=qo, blk_out=qb, with_frames=False)
         lf.lf_qk_prologue(kc, gamma, g, nq, f0, lat_w, x_out=ko, blk_out=kb, frm_out=kf)
 
     n = max(5, min(args.steps, 50))
-    t_fused = per_call(fused, n)
+    t_step = per_call(one_launch, n)
+    t_two = per_call(two_calls, n)
     t_pool = per_call(lambda: lf.lf_pool_qk(qo, ko, g, nq, nq, qb, kb, kf), n)
     esz = 2 if w.dtype == "bf16" else 4
     tokens = 2 * w.B * w.H * nq * tpf
-    moved = tokens * w.d * esz * 2 + 2 * w.B * w.H * nq * nb * w.d * 4 + w.B * w.H * nq * w.d * 4
-    return {"what": f"queries and the chunk's own {nq} key frames: RMSNorm + rotary + block/frame means",
-            "lat_w": lat_w, "fused_us": round(t_fused, 2), "hbm_gbs": round(moved / (t_fused * 1e-6) / 1e9, 1),
+    moved = tokens * w.d * esz * 2 + 2 * w.B * w.H * nq * nb * w.d * 4 + lag_bytes(w, n_lag)
+    moved_two = tokens * w.d * esz * 2 + 2 * w.B * w.H * nq * nb * w.d * 4 + w.B * w.H * nq * w.d * 4
+    return {"what": (f"queries and the chunk's own {nq} key frames: RMSNorm + rotary + block means, with the "
+                     f"previous chunk's {n_lag} frame means, in one launch"),
+            "lat_w": lat_w, "fused_us": round(t_step, 2), "hbm_gbs": round(moved / (t_step * 1e-6) / 1e9, 1),
+            "algorithmic_bytes": moved,
+            "two_calls_us": round(t_two, 2), "two_calls_hbm_gbs": round(moved_two / (t_two * 1e-6) / 1e9, 1),
             "separate_pool_pass_us": round(t_pool, 2)}
 
 

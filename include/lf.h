@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define LF_ABI_VERSION 3
+#define LF_ABI_VERSION 4
 
 typedef enum {
   LF_OK = 0,
@@ -175,6 +175,52 @@ lf_status lf_pool_qk(const void* q, const void* k, lf_dtype dt, lf_geom g, int32
 lf_status lf_qk_prologue(const void* x, void* x_out, const float* gamma, lf_dtype dt, lf_geom g,
                          int32_t n_frames, int32_t frame0, int32_t lat_w, float eps, float theta,
                          float* blk_out, float* frm_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * lf_pool_step -- [S2] the pooling of one chunk in steady state, in one launch. A frame's
+ * keys do not change once it is in the KV cache, so its block and frame means are kept in
+ * a pooled-key cache; each call pools the chunk's queries and only its new key frames.
+ * The chunk's own frames are always kept by [S3] (current-chunk frames), so their frame
+ * means are first read by the next chunk's frame stage: this call leaves them out and
+ * instead forms the frame means of n_lag earlier frames (normally the previous chunk's)
+ * from block means that an earlier call wrote, in the same launch.
+ *   q_blk  <- block means of q (n_qframes frames; packed [B, H, n_qframes*n_bpf, d] fp32)
+ *   k_blk  <- block means of k_new at cache frames [f_new, f_new + n_new)
+ *   k_frm  <- frame means of cache frames [f_lag, f_lag + n_lag), from k_blk
+ * q: [B, H, n_qframes*tpf, d], slices g.head_stride tokens apart (0 = packed); k_new:
+ *   [B, H, n_new*tpf, d], slices g.kv_head_stride apart (0 = packed); dtype dt.
+ * k_blk, k_frm: the pooled-key cache at frame 0 ([B, H, frames*n_bpf, d] and
+ *   [B, H, frames, d] fp32), slices g.frame_stride frames apart; g.frame_stride is the
+ *   cache's frame count and must be >= 1 (no packed form here).
+ * Results are bitwise those of lf_pool / lf_pool_qk over the same frames. n_qframes,
+ * n_new and n_lag may each be 0 (the matching pointers may then be NULL); with all three 0
+ * the call does nothing. The two frame ranges must lie in the cache and be disjoint.
+ * Limits and errors: those of lf_pool_qk.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_pool_step(const void* q, const void* k_new, lf_dtype dt, lf_geom g, int32_t n_qframes,
+                       int32_t n_new, int32_t f_new, int32_t f_lag, int32_t n_lag, float* q_blk,
+                       float* k_blk, float* k_frm, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * lf_qk_prologue_step -- lf_qk_prologue of a chunk's queries and of its new keys in one
+ * launch, with the pooling of lf_pool_step: q_out = RoPE(RMSNorm(q; gamma_q)) and
+ * k_out = RoPE(RMSNorm(k_new; gamma_k)) (both at clip frames frame0 .. frame0 +
+ * n_frames - 1, lat_w tokens per latent row), q_blk <- block means of q_out, k_blk <-
+ * block means of k_out at cache frames [f_new, f_new + n_frames), k_frm <- frame means of
+ * cache frames [f_lag, f_lag + n_lag) from k_blk (n_lag may be 0, k_frm then NULL).
+ * Every output is bitwise what lf_qk_prologue of each tensor (without frame means) gives.
+ * q, k_new, q_out: [B, H, n_frames*tpf, d], slices g.head_stride tokens apart; k_out:
+ *   the same shape, slices g.kv_head_stride apart (a KV cache view); dtype dt; outputs
+ *   must not alias inputs. gamma_q, gamma_k: [d] fp32.
+ * k_blk, k_frm, g.frame_stride: as for lf_pool_step. eps, theta, lat_w: as for
+ *   lf_qk_prologue.
+ * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED (d, dtype), LF_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+lf_status lf_qk_prologue_step(const void* q, const void* k_new, void* q_out, void* k_out,
+                              const float* gamma_q, const float* gamma_k, lf_dtype dt, lf_geom g,
+                              int32_t n_frames, int32_t frame0, int32_t lat_w, float eps, float theta,
+                              int32_t f_new, int32_t f_lag, int32_t n_lag, float* q_blk, float* k_blk,
+                              float* k_frm, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * lf_select_frames -- [S3] frame stage: for every row (b, h, query block r), the frame

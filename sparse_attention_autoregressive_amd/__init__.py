@@ -15,8 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["Geom", "LfError", "lf_abi_version", "lf_cag_schedule", "lf_block_budget",
-           "lf_pool", "lf_pool_qk", "lf_qk_prologue", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_select_blocks_1d", "lf_sparse_attn",
-           "lf_probe_mfma_bf16", "library_path", "n_bpf"]
+           "lf_pool", "lf_pool_qk", "lf_pool_step", "lf_qk_prologue", "lf_qk_prologue_step", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_select_blocks_1d", "lf_sparse_attn",
+           "lf_probe_mfma_bf16", "lf_probe_hbm_read", "library_path", "n_bpf"]
 
 LF_OK, LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_INFEASIBLE, LF_ERR_HIP = range(5)
 LF_FP32, LF_BF16 = 0, 1
@@ -98,7 +98,11 @@ def _load():
         "lf_sparse_attn": [vp, vp, vp, vp, i32, Geom, i32, i32, vp, i32, f32, vp],
         "lf_select_blocks_1d": [vp, vp, Geom, i32, i32, i32, vp, vp],
         "lf_qk_prologue": [vp, vp, vp, i32, Geom, i32, i32, i32, f32, f32, vp, vp, vp],
+        "lf_pool_step": [vp, vp, i32, Geom, i32, i32, i32, i32, i32, vp, vp, vp, vp],
+        "lf_qk_prologue_step": [vp, vp, vp, vp, vp, vp, i32, Geom, i32, i32, i32, f32, f32, i32, i32, i32, vp, vp,
+                                vp, vp],
         "lf_probe_mfma_bf16": [i32, i32, vp, vp, vp],
+        "lf_probe_hbm_read": [vp, ctypes.c_int64, i32, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -296,6 +300,77 @@ def lf_qk_prologue(x: torch.Tensor, gamma: torch.Tensor, g: Geom, n_frames: int,
     return x_out, blk_out, frm_out
 
 
+def _cache(k_blk: torch.Tensor, k_frm: torch.Tensor, g: Geom) -> int:
+    """Checks a pooled-key cache pair (block means [B, H, frames*n_bpf, d], frame means
+    [B, H, frames, d], fp32, each (b, h) slice contiguous); returns its frame count."""
+    nb = n_bpf(g)
+    frames = k_frm.shape[2] if isinstance(k_frm, torch.Tensor) and k_frm.dim() == 4 else -1
+    if frames < 1:
+        raise ValueError("k_frm must be [B, H, frames, d]")
+    if _pooled(k_blk, "k_blk", g, frames, nb) != frames or _pooled(k_frm, "k_frm", g, frames, 1) != frames:
+        raise ValueError("the pooled-key cache tensors must be whole (not views of a bigger cache)")
+    return frames
+
+
+def lf_pool_step(q: Optional[torch.Tensor], k_new: Optional[torch.Tensor], g: Geom, n_qframes: int, n_new: int,
+                 f_new: int, f_lag: int, n_lag: int, q_blk: Optional[torch.Tensor], k_blk: torch.Tensor,
+                 k_frm: torch.Tensor):
+    """One steady-state pooling launch: q_blk <- block means of q, k_blk[frames f_new..] <-
+    block means of k_new, k_frm[frames f_lag..f_lag+n_lag) <- frame means from k_blk
+    (k_blk, k_frm: a whole pooled-key cache). Returns q_blk."""
+    lib = _load()
+    nb = n_bpf(g)
+    frames = _cache(k_blk, k_frm, g)
+    dev = k_blk.device
+    if n_qframes > 0 and q_blk is None:
+        q_blk = torch.empty((g.B, g.H, n_qframes * nb, g.d), dtype=torch.float32, device=dev)
+    lq, lk = n_qframes * g.tokens_per_frame, n_new * g.tokens_per_frame
+    hs = _shared("q", [_tokens(q, "q", g, lq)], lq) if n_qframes > 0 else 0
+    ks = _shared("k_new", [_tokens(k_new, "k_new", g, lk)], lk) if n_new > 0 else 0
+    dtc = _dtype_code(q if n_qframes > 0 else (k_new if n_new > 0 else k_blk))
+    if n_qframes > 0 and n_new > 0 and q.dtype != k_new.dtype:
+        raise TypeError("q and k_new must share a dtype")
+    qp = _exact(q_blk, "q_blk", torch.float32, (g.B, g.H, n_qframes * nb, g.d)) if n_qframes > 0 else None
+    gg = g.with_stride(hs, ks).with_frame_stride(frames)
+    _check(lib.lf_pool_step(q.data_ptr() if n_qframes > 0 else None, k_new.data_ptr() if n_new > 0 else None, dtc, gg,
+                            n_qframes, n_new, f_new, f_lag, n_lag, qp, k_blk.data_ptr(), k_frm.data_ptr(),
+                            _stream(k_blk)))
+    return q_blk
+
+
+def lf_qk_prologue_step(q: torch.Tensor, k_new: torch.Tensor, gamma_q: torch.Tensor, gamma_k: torch.Tensor, g: Geom,
+                        n_frames: int, frame0: int, lat_w: int, f_new: int, f_lag: int, n_lag: int,
+                        k_out: torch.Tensor, k_blk: torch.Tensor, k_frm: torch.Tensor, eps: float = 1e-6,
+                        theta: float = 10000.0, q_out: Optional[torch.Tensor] = None,
+                        q_blk: Optional[torch.Tensor] = None):
+    """RMSNorm + rotary of a chunk's queries and new keys in one launch (keys written to
+    k_out, e.g. a KV cache view), with the block means of both and the lagged frame means
+    of lf_pool_step. Returns (q_out, q_blk)."""
+    lib = _load()
+    nb = n_bpf(g)
+    frames = _cache(k_blk, k_frm, g)
+    L = n_frames * g.tokens_per_frame
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if q_blk is None:
+        q_blk = torch.empty((g.B, g.H, n_frames * nb, g.d), dtype=torch.float32, device=q.device)
+    if not (q.dtype == k_new.dtype == q_out.dtype == k_out.dtype):
+        raise TypeError("q, k_new, q_out and k_out must share a dtype")
+    for name, gm in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if gm.dtype != torch.float32 or tuple(gm.shape) != (g.d,):
+            raise ValueError(f"{name} must be float32 of shape ({g.d},)")
+    hs = _shared("q, k_new and q_out", [_tokens(q, "q", g, L), _tokens(k_new, "k_new", g, L),
+                                        _tokens(q_out, "q_out", g, L)], L)
+    ks = _shared("k_out", [_tokens(k_out, "k_out", g, L)], L)
+    gg = g.with_stride(hs, ks).with_frame_stride(frames)
+    _check(lib.lf_qk_prologue_step(q.data_ptr(), k_new.data_ptr(), q_out.data_ptr(), k_out.data_ptr(),
+                                   _dev(gamma_q, "gamma_q"), _dev(gamma_k, "gamma_k"), _dtype_code(q), gg, n_frames,
+                                   frame0, lat_w, float(eps), float(theta), f_new, f_lag, n_lag,
+                                   _exact(q_blk, "q_blk", torch.float32, (g.B, g.H, n_frames * nb, g.d)),
+                                   k_blk.data_ptr(), k_frm.data_ptr(), _stream(q)))
+    return q_out, q_blk
+
+
 def lf_select_frames(q_blk: torch.Tensor, k_frm: torch.Tensor, g: Geom, n_qb: int, n_kframes: int,
                      mem: Sequence[int], forced: Sequence[int], k_f: int,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -396,3 +471,12 @@ def lf_probe_mfma_bf16(n_wg: int, iters: int, sink: torch.Tensor, clocks: torch.
     if clocks.dtype != torch.int64 or clocks.numel() < 2:
         raise ValueError("clocks must be int64 with 2 entries")
     _check(_load().lf_probe_mfma_bf16(n_wg, iters, _dev(sink, "sink"), _dev(clocks, "clocks"), _stream(sink)))
+
+
+def lf_probe_hbm_read(x: torch.Tensor, n_wg: int, sink: torch.Tensor) -> None:
+    """Enqueues a plain streaming read of all of x's bytes (include/lf_probe.h) on the
+    current stream; sink: float32 [n_wg * 256]."""
+    if sink.dtype != torch.float32 or sink.numel() < n_wg * 256:
+        raise ValueError("sink must be float32 with n_wg * 256 entries")
+    _check(_load().lf_probe_hbm_read(_dev(x, "x"), x.numel() * x.element_size(), n_wg, _dev(sink, "sink"),
+                                     _stream(x)))

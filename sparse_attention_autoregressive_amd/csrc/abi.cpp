@@ -136,6 +136,35 @@ lf_status check_block_stage(const float* k_blk, lf_geom g, int32_t n_qb, int32_t
   return LF_OK;
 }
 
+// Checks shared by the steady-state step calls: the cache geometry and the two frame
+// ranges (new frames and lagged frames), both inside the cache and disjoint.
+lf_status check_step_frames(const lf_geom& g, int32_t n_new, int32_t f_new, int32_t f_lag, int32_t n_lag, int* stride,
+                            const char* fn) {
+  if (n_new < 0 || f_new < 0 || f_lag < 0 || n_lag < 0)
+    return fail(LF_ERR_INVALID_ARG, "%s: negative frame index or count", fn);
+  if (g.frame_stride < 1) return fail(LF_ERR_INVALID_ARG, "%s: frame_stride must give the cache's frame count", fn);
+  if (static_cast<long long>(f_new) + n_new > g.frame_stride || static_cast<long long>(f_lag) + n_lag > g.frame_stride)
+    return fail(LF_ERR_INVALID_ARG, "%s: frames beyond the cache's %d frames", fn, g.frame_stride);
+  if (n_new > 0 && n_lag > 0 && f_lag < f_new + n_new && f_new < f_lag + n_lag)
+    return fail(LF_ERR_INVALID_ARG, "%s: lagged frames [%d, %d) overlap the new frames [%d, %d)", fn, f_lag,
+                f_lag + n_lag, f_new, f_new + n_new);
+  *stride = g.frame_stride;
+  return LF_OK;
+}
+
+// The rotary turn (revolutions per unit of position) of each pair: pair k turns with the
+// token's frame for the first d/2 - 2*floor(d/6) pairs, then its row, then its column;
+// pair i of an axis with n pairs turns theta^(-i/n) radians per unit.
+void rotary_turns(int d, float theta, float* rev) {
+  const int n_hw = d / 6, n_t = d / 2 - 2 * n_hw;
+  for (int k = 0; k < d / 2; ++k) {
+    const int i = k < n_t ? k : (k < n_t + n_hw ? k - n_t : k - n_t - n_hw);
+    const int n = k < n_t ? n_t : n_hw;
+    rev[k] = static_cast<float>(std::pow(static_cast<double>(theta), -static_cast<double>(i) / n) /
+                                (2.0 * 3.14159265358979323846));
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,17 +332,121 @@ lf_status lf_qk_prologue(const void* x, void* x_out, const float* gamma, lf_dtyp
   a.n_bpf = n_bpf;
   a.lat_w = lat_w;
   a.eps = eps;
-  // pair k: axis frame for the first d/2 - 2*floor(d/6) pairs, then row, then column;
-  // pair i of an axis with n pairs turns theta^(-i/n) radians per unit of position
-  const int n_hw = g.d / 6, n_t = g.d / 2 - 2 * n_hw;
-  for (int k = 0; k < g.d / 2; ++k) {
-    const int i = k < n_t ? k : (k < n_t + n_hw ? k - n_t : k - n_t - n_hw);
-    const int n = k < n_t ? n_t : n_hw;
-    a.rev[k] = static_cast<float>(std::pow(static_cast<double>(theta), -static_cast<double>(i) / n) /
-                                  (2.0 * 3.14159265358979323846));
-  }
+  rotary_turns(g.d, theta, a.rev);
   pending_error();
   return hip_status(lf::launch_prologue(a, dt == LF_BF16, g.d, static_cast<hipStream_t>(stream)), fn);
+}
+
+lf_status lf_pool_step(const void* q, const void* k_new, lf_dtype dt, lf_geom g, int32_t n_qframes, int32_t n_new,
+                       int32_t f_new, int32_t f_lag, int32_t n_lag, float* q_blk, float* k_blk, float* k_frm,
+                       void* stream) {
+  const char* fn = "lf_pool_step";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (dt != LF_FP32 && dt != LF_BF16) return fail(LF_ERR_UNSUPPORTED, "%s: dtype %d unsupported", fn, (int)dt);
+  if (n_qframes < 0) return fail(LF_ERR_INVALID_ARG, "%s: n_qframes must be >= 0", fn);
+  int cs = 0;
+  if (lf_status st = check_step_frames(g, n_new, f_new, f_lag, n_lag, &cs, fn)) return st;
+  if ((n_qframes > 0 && (!q || !q_blk)) || (n_new > 0 && !k_new) || ((n_new > 0 || n_lag > 0) && !k_blk) ||
+      (n_lag > 0 && !k_frm))
+    return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if ((q && !aligned16(q)) || (k_new && !aligned16(k_new)) || (q_blk && !aligned16(q_blk)) ||
+      (k_blk && !aligned16(k_blk)) || (k_frm && !aligned16(k_frm)))
+    return fail(LF_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const int n_bpf = n_bpf_of(g);
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  const long long lq = static_cast<long long>(n_qframes) * g.tokens_per_frame;
+  const long long lk = static_cast<long long>(n_new) * g.tokens_per_frame;
+  if (!fits_int(BH * (n_qframes + static_cast<long long>(n_new)) * n_bpf) || !fits_int(BH * cs * n_bpf) ||
+      !fits_int(BH * cs * static_cast<long long>(g.d)) || !fits_int(lq) || !fits_int(lk))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  if (g.head_stride != 0 && g.head_stride < lq)
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < query token count %lld", fn, g.head_stride, lq);
+  if (g.kv_head_stride != 0 && g.kv_head_stride < lk)
+    return fail(LF_ERR_INVALID_ARG, "%s: kv_head_stride %d < new key token count %lld", fn, g.kv_head_stride, lk);
+  if (n_qframes == 0 && n_new == 0 && n_lag == 0) return LF_OK;     // nothing to do
+  lf::PoolStepArgs a;
+  a.q = q;
+  a.k = k_new;
+  a.q_blk = q_blk;
+  a.k_blk = k_blk;
+  a.k_frm = k_frm;
+  a.q_stride = g.head_stride ? g.head_stride : lq;
+  a.k_stride = g.kv_head_stride ? g.kv_head_stride : lk;
+  a.BH = static_cast<int>(BH);
+  a.n_qframes = n_qframes;
+  a.n_new = n_new;
+  a.f_new = f_new;
+  a.f_lag = f_lag;
+  a.n_lag = n_lag;
+  a.cache_stride = cs;
+  a.tpf = g.tokens_per_frame;
+  a.bs = g.block_size;
+  a.n_bpf = n_bpf;
+  pending_error();
+  return hip_status(lf::launch_pool_step(a, dt == LF_BF16, g.d, static_cast<hipStream_t>(stream)), fn);
+}
+
+lf_status lf_qk_prologue_step(const void* q, const void* k_new, void* q_out, void* k_out, const float* gamma_q,
+                              const float* gamma_k, lf_dtype dt, lf_geom g, int32_t n_frames, int32_t frame0,
+                              int32_t lat_w, float eps, float theta, int32_t f_new, int32_t f_lag, int32_t n_lag,
+                              float* q_blk, float* k_blk, float* k_frm, void* stream) {
+  const char* fn = "lf_qk_prologue_step";
+  if (lf_status st = check_geom(g, fn)) return st;
+  if (dt != LF_FP32 && dt != LF_BF16) return fail(LF_ERR_UNSUPPORTED, "%s: dtype %d unsupported", fn, (int)dt);
+  if (n_frames < 1 || frame0 < 0) return fail(LF_ERR_INVALID_ARG, "%s: n_frames must be >= 1 and frame0 >= 0", fn);
+  if (lat_w < 1 || g.tokens_per_frame % lat_w != 0)
+    return fail(LF_ERR_INVALID_ARG, "%s: lat_w=%d must divide tokens_per_frame=%d", fn, lat_w, g.tokens_per_frame);
+  if (!(std::isfinite(eps) && eps > 0.f)) return fail(LF_ERR_INVALID_ARG, "%s: eps must be finite and > 0", fn);
+  if (!(std::isfinite(theta) && theta > 1.f)) return fail(LF_ERR_INVALID_ARG, "%s: theta must be finite and > 1", fn);
+  int cs = 0;
+  if (lf_status st = check_step_frames(g, n_frames, f_new, f_lag, n_lag, &cs, fn)) return st;
+  if (!q || !k_new || !q_out || !k_out || !gamma_q || !gamma_k || !q_blk || !k_blk || (n_lag > 0 && !k_frm))
+    return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(gamma_q) ||
+      !aligned16(gamma_k) || !aligned16(q_blk) || !aligned16(k_blk) || (k_frm && !aligned16(k_frm)))
+    return fail(LF_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  if (q == q_out || k_new == k_out) return fail(LF_ERR_INVALID_ARG, "%s: outputs must not alias inputs", fn);
+  const int n_bpf = n_bpf_of(g);
+  const long long BH = static_cast<long long>(g.B) * g.H;
+  const long long len = static_cast<long long>(n_frames) * g.tokens_per_frame;
+  if (!fits_int(BH * 2 * n_frames * n_bpf) || !fits_int(BH * cs * n_bpf) || !fits_int(BH * cs * static_cast<long long>(g.d)) ||
+      !fits_int(len) || !fits_int(frame0 + static_cast<long long>(n_frames)))
+    return fail(LF_ERR_INVALID_ARG, "%s: problem too large", fn);
+  if (g.head_stride != 0 && g.head_stride < len)
+    return fail(LF_ERR_INVALID_ARG, "%s: head_stride %d < n_frames*tpf = %lld", fn, g.head_stride, len);
+  if (g.kv_head_stride != 0 && g.kv_head_stride < len)
+    return fail(LF_ERR_INVALID_ARG, "%s: kv_head_stride %d < n_frames*tpf = %lld", fn, g.kv_head_stride, len);
+  lf::ProlArgs a;
+  a.x = q;
+  a.y = q_out;
+  a.gamma = gamma_q;
+  a.blk = q_blk;
+  a.frm = nullptr;
+  a.x_stride = g.head_stride ? g.head_stride : len;
+  a.y_stride = a.x_stride;
+  a.BH = static_cast<int>(BH);
+  a.n_frames = n_frames;
+  a.frame0 = frame0;
+  a.out_stride = n_frames;
+  a.tpf = g.tokens_per_frame;
+  a.bs = g.block_size;
+  a.n_bpf = n_bpf;
+  a.lat_w = lat_w;
+  a.eps = eps;
+  rotary_turns(g.d, theta, a.rev);
+  lf::ProlStepArgs s;
+  s.k = k_new;
+  s.k_out = k_out;
+  s.gamma_k = gamma_k;
+  s.k_blk = k_blk;
+  s.k_frm = k_frm;
+  s.k_out_stride = g.kv_head_stride ? g.kv_head_stride : len;
+  s.cache_stride = cs;
+  s.f_new = f_new;
+  s.f_lag = f_lag;
+  s.n_lag = n_lag;
+  pending_error();
+  return hip_status(lf::launch_prologue_step(a, s, dt == LF_BF16, g.d, static_cast<hipStream_t>(stream)), fn);
 }
 
 lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
@@ -447,6 +580,16 @@ lf_status lf_probe_mfma_bf16(int32_t n_wg, int32_t iters, float* sink, int64_t* 
   return hip_status(lf::launch_mfma_probe(n_wg, iters, sink, reinterpret_cast<long long*>(clocks),
                                           static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+lf_status lf_probe_hbm_read(const void* x, int64_t bytes, int32_t n_wg, float* sink, void* stream) {
+  const char* fn = "lf_probe_hbm_read";
+  if (n_wg < 1) return fail(LF_ERR_INVALID_ARG, "%s: n_wg must be >= 1", fn);
+  if (bytes <= 0 || (bytes % 16) != 0) return fail(LF_ERR_INVALID_ARG, "%s: bytes must be a positive multiple of 16", fn);
+  if (!x || !sink) return fail(LF_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
+  pending_error();
+  return hip_status(lf::launch_hbm_read(x, bytes, n_wg, sink, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

@@ -46,6 +46,33 @@ struct ProlArgs {
 };
 hipError_t launch_prologue(const ProlArgs& a, bool bf16, int d, hipStream_t st);
 
+// The keys' half of a steady-state prologue step (ProlArgs describes the queries; both
+// share frames, positions and geometry) and the lagged frame means of a pooled-key cache.
+struct ProlStepArgs {
+  const void* k;          // the chunk's new keys, (b, h) slices ProlArgs::x_stride tokens apart
+  void* k_out;            // where they go (a KV cache view), slices k_out_stride tokens apart
+  const float* gamma_k;   // [d]
+  float* k_blk;           // pooled-key cache, frame 0 (slices cache_stride frames apart)
+  float* k_frm;
+  long long k_out_stride;
+  int cache_stride, f_new, f_lag, n_lag;
+};
+hipError_t launch_prologue_step(const ProlArgs& a, const ProlStepArgs& s, bool bf16, int d, hipStream_t st);
+
+// Pooling of one steady-state step: query block means, the new key frames' block means
+// into a pooled-key cache at frame f_new, and the frame means of cache frames
+// [f_lag, f_lag + n_lag) from block means an earlier launch wrote, in one launch.
+struct PoolStepArgs {
+  const void* q;
+  const void* k;
+  float* q_blk;
+  float* k_blk;           // cache, frame 0
+  float* k_frm;
+  long long q_stride, k_stride;
+  int BH, n_qframes, n_new, f_new, f_lag, n_lag, cache_stride, tpf, bs, n_bpf;
+};
+hipError_t launch_pool_step(const PoolStepArgs& a, bool bf16, int d, hipStream_t st);
+
 struct SelectArgs {
   const float* q_blk;
   const float* k_frm;
@@ -90,5 +117,7 @@ hipError_t launch_select_1d(const Select1DArgs& a, int d, int n_rows, hipStream_
 
 // Dense bf16 MFMA loop of n_wg 4-wave workgroups (measurement aid).
 hipError_t launch_mfma_probe(int n_wg, int iters, float* sink, long long* clocks, hipStream_t st);
+// Streaming read of `bytes` (a multiple of 16) by n_wg 256-thread workgroups (measurement aid).
+hipError_t launch_hbm_read(const void* x, long long bytes, int n_wg, float* sink, hipStream_t st);
 
 }  // namespace lf

@@ -62,7 +62,20 @@ __device__ __forceinline__ float token_lane_sum(float x) {
 // Sums of block j of a frame (the frame's tokens [j*bs, j*bs + len)) into `sum`,
 // valid in lanes < C (lane c holds chunk c). Up to kBatch tokens per lane are loaded
 // before any is added, so a wave keeps kBatch * 1 KB in flight.
+//
+// Summation order (shared with the prologue, whose four waves each take one quarter):
+// load u of every batch goes to the lane's accumulator set q = u / kQuarter, added in
+// batch and u order; the four sets are combined as ((A0 + A1) + (A2 + A3)); then the
+// token lanes' sums are added by the fixed butterfly.
 constexpr int kBatch = 16;
+constexpr int kQuarters = 4;
+constexpr int kQuarter = kBatch / kQuarters;
+
+template <int E, int C>
+__device__ __forceinline__ void combine_quarters(const float (&A)[kQuarters][E], float* sum) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) sum[e] = token_lane_sum<C>((A[0][e] + A[1][e]) + (A[2][e] + A[3][e]));
+}
 
 template <typename T, int D>
 __device__ __forceinline__ void block_sum(const T* __restrict__ frame, int j, int bs, int len, int lane,
@@ -72,9 +85,11 @@ __device__ __forceinline__ void block_sum(const T* __restrict__ frame, int j, in
   constexpr int TL = kWave / C;
   const int c = lane % C, s = lane / C;
   const T* base = frame + static_cast<size_t>(j) * bs * D + c * E;
-  float a[E], b[E];
+  float A[kQuarters][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) a[e] = b[e] = 0.f;
+  for (int q = 0; q < kQuarters; ++q)
+#pragma unroll
+    for (int e = 0; e < E; ++e) A[q][e] = 0.f;
   for (int t0 = 0; t0 < len; t0 += kBatch * TL) {
     uint4 v[kBatch];
 #pragma unroll
@@ -83,10 +98,9 @@ __device__ __forceinline__ void block_sum(const T* __restrict__ frame, int j, in
       v[u] = t < len ? *reinterpret_cast<const uint4*>(base + static_cast<size_t>(t) * D) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) Chunk16<T>::add(reinterpret_cast<const T*>(&v[u]), (u & 1) ? b : a);
+    for (int u = 0; u < kBatch; ++u) Chunk16<T>::add(reinterpret_cast<const T*>(&v[u]), A[u / kQuarter]);
   }
-#pragma unroll
-  for (int e = 0; e < E; ++e) sum[e] = token_lane_sum<C>(a[e] + b[e]);
+  combine_quarters<E, C>(A, sum);
 }
 
 // One tensor's share of a block-mean launch: n_blocks = BH * n_frames * n_bpf blocks,
@@ -119,10 +133,45 @@ __device__ __forceinline__ void pool_block(const PoolJob<T>& p, int b, int tpf, 
   }
 }
 
-// Wave w of the grid pools block w of the list "a's blocks, then b's blocks".
+// The frame mean of one channel of one frame: the frame's block means, each weighted by
+// its token count, added in block order, divided by the frame's token count. `slot` is
+// the frame's index in the pooled tensors (b, h slice offset included).
+template <int D>
+__device__ __forceinline__ void frame_mean_channel(const float* __restrict__ blk, float* __restrict__ frm,
+                                                   size_t slot, int c, int tpf, int bs, int n_bpf) {
+  const float* row = blk + slot * n_bpf * D + c;
+  float s = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < n_bpf; ++j) s += row[static_cast<size_t>(j) * D] * static_cast<float>(min(bs, tpf - j * bs));
+  frm[slot * D + c] = s / static_cast<float>(tpf);
+}
+
+// Frame means of frames [f0, f0 + n_frames) of every (b, h) slice of a pooled-key cache
+// (slices out_stride frames apart) whose block means an earlier launch wrote: one thread
+// per (slice frame, channel), n_items = BH * n_frames * D.
+struct LagJob {
+  const float* blk;
+  float* frm;
+  int f0, n_frames, out_stride, n_items;
+};
+
+template <int D>
+__device__ __forceinline__ void lag_item(const LagJob& L, int t, int tpf, int bs, int n_bpf) {
+  if (t >= L.n_items) return;
+  const int bf = t / D, c = t % D;
+  const int bh = bf / L.n_frames, f = L.f0 + (bf - bh * L.n_frames);
+  frame_mean_channel<D>(L.blk, L.frm, static_cast<size_t>(bh) * L.out_stride + f, c, tpf, bs, n_bpf);
+}
+
+// Wave w of the first block_wgs workgroups pools block w of the list "a's blocks, then
+// b's blocks"; the workgroups after them form the frame means of the lag job.
 template <typename T, int D>
-__global__ void __launch_bounds__(kPoolWaves * kWave) block_mean_kernel(PoolJob<T> a, PoolJob<T> b, int tpf, int bs,
-                                                                        int n_bpf) {
+__global__ void __launch_bounds__(kPoolWaves * kWave) block_mean_kernel(PoolJob<T> a, PoolJob<T> b, LagJob lag,
+                                                                        int block_wgs, int tpf, int bs, int n_bpf) {
+  if (static_cast<int>(blockIdx.x) >= block_wgs) {
+    lag_item<D>(lag, (blockIdx.x - block_wgs) * (kPoolWaves * kWave) + threadIdx.x, tpf, bs, n_bpf);
+    return;
+  }
   const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kPoolWaves + threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   if (w < a.n_blocks)
@@ -131,8 +180,8 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) block_mean_kernel(PoolJob<
     pool_block<T, D>(b, w - a.n_blocks, tpf, bs, n_bpf, lane);
 }
 
-// Thread (frame, channel): the frame mean from the frame's block means, each weighted
-// by its token count, added in block order. n_slices_frames = BH * n_frames.
+// Thread (frame, channel): frame_mean_channel for every frame of a launch.
+// n_slices_frames = BH * n_frames.
 template <int D>
 __global__ void __launch_bounds__(kFrameThreads) frame_mean_kernel(const float* __restrict__ blk,
                                                                    float* __restrict__ frm, int n_slice_frames,
@@ -142,20 +191,21 @@ __global__ void __launch_bounds__(kFrameThreads) frame_mean_kernel(const float* 
   const int bf = t / D, c = t % D;
   if (bf >= n_slice_frames) return;
   const int bh = bf / n_frames, f = bf - bh * n_frames;
-  const size_t slot = static_cast<size_t>(bh) * out_stride + f;
-  const float* row = blk + slot * n_bpf * D + c;
-  float s = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < n_bpf; ++j) s += row[static_cast<size_t>(j) * D] * static_cast<float>(min(bs, tpf - j * bs));
-  frm[slot * D + c] = s / static_cast<float>(tpf);
+  frame_mean_channel<D>(blk, frm, static_cast<size_t>(bh) * out_stride + f, c, tpf, bs, n_bpf);
+}
+
+template <int D>
+static unsigned lag_wgs(const LagJob& lag) {
+  return static_cast<unsigned>((lag.n_items + kPoolWaves * kWave - 1) / (kPoolWaves * kWave));
 }
 
 template <typename T, int D>
-static hipError_t launch_t(PoolJob<T> a, PoolJob<T> b, float* frm, int BH, int tpf, int bs, int n_bpf,
+static hipError_t launch_t(PoolJob<T> a, PoolJob<T> b, float* frm, LagJob lag, int BH, int tpf, int bs, int n_bpf,
                            hipStream_t st) {
   const unsigned waves = static_cast<unsigned>(a.n_blocks) + static_cast<unsigned>(b.n_blocks);
-  hipLaunchKernelGGL((block_mean_kernel<T, D>), dim3((waves + kPoolWaves - 1) / kPoolWaves),
-                     dim3(kPoolWaves * kWave), 0, st, a, b, tpf, bs, n_bpf);
+  const unsigned bwgs = (waves + kPoolWaves - 1) / kPoolWaves;
+  hipLaunchKernelGGL((block_mean_kernel<T, D>), dim3(bwgs + lag_wgs<D>(lag)), dim3(kPoolWaves * kWave), 0, st, a, b, lag,
+                     static_cast<int>(bwgs), tpf, bs, n_bpf);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (frm == nullptr) return hipSuccess;
   // frame means of b (the keys)
@@ -172,11 +222,13 @@ static PoolJob<T> job(const void* x, float* blk, int BH, int n_frames, int n_bpf
   return PoolJob<T>{static_cast<const T*>(x), blk, x_stride, n_frames, out_stride, BH * n_frames * n_bpf};
 }
 
+static LagJob no_lag() { return LagJob{nullptr, nullptr, 0, 1, 1, 0}; }
+
 template <typename T>
-static hipError_t launch_d(int d, PoolJob<T> a, PoolJob<T> b, float* frm, int BH, int tpf, int bs, int n_bpf,
-                           hipStream_t st) {
-  return d == 128 ? launch_t<T, 128>(a, b, frm, BH, tpf, bs, n_bpf, st)
-                  : launch_t<T, 64>(a, b, frm, BH, tpf, bs, n_bpf, st);
+static hipError_t launch_d(int d, PoolJob<T> a, PoolJob<T> b, float* frm, LagJob lag, int BH, int tpf, int bs,
+                           int n_bpf, hipStream_t st) {
+  return d == 128 ? launch_t<T, 128>(a, b, frm, lag, BH, tpf, bs, n_bpf, st)
+                  : launch_t<T, 64>(a, b, frm, lag, BH, tpf, bs, n_bpf, st);
 }
 
 hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH, int n_qframes, int n_kframes,
@@ -184,11 +236,11 @@ hipError_t launch_pool_qk(const void* q, const void* k, bool bf16, int d, int BH
                           float* q_blk, float* k_blk, float* k_frm, hipStream_t st) {
   if (bf16)
     return launch_d<__bf16>(d, job<__bf16>(q, q_blk, BH, n_qframes, n_bpf, q_stride, n_qframes),
-                            job<__bf16>(k, k_blk, BH, n_kframes, n_bpf, k_stride, k_out_stride), k_frm, BH, tpf, bs,
-                            n_bpf, st);
+                            job<__bf16>(k, k_blk, BH, n_kframes, n_bpf, k_stride, k_out_stride), k_frm, no_lag(), BH,
+                            tpf, bs, n_bpf, st);
   return launch_d<float>(d, job<float>(q, q_blk, BH, n_qframes, n_bpf, q_stride, n_qframes),
-                         job<float>(k, k_blk, BH, n_kframes, n_bpf, k_stride, k_out_stride), k_frm, BH, tpf, bs,
-                         n_bpf, st);
+                         job<float>(k, k_blk, BH, n_kframes, n_bpf, k_stride, k_out_stride), k_frm, no_lag(), BH, tpf,
+                         bs, n_bpf, st);
 }
 
 hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, int tpf, int bs,
@@ -196,10 +248,23 @@ hipError_t launch_pool(const void* x, bool bf16, int d, int BH, int n_frames, in
   // a single tensor rides in the second slot (the one whose frame means are formed)
   if (bf16)
     return launch_d<__bf16>(d, PoolJob<__bf16>{nullptr, nullptr, 0, 1, 1, 0},
-                            job<__bf16>(x, blk, BH, n_frames, n_bpf, x_stride, out_stride), frm, BH, tpf, bs, n_bpf,
-                            st);
+                            job<__bf16>(x, blk, BH, n_frames, n_bpf, x_stride, out_stride), frm, no_lag(), BH, tpf, bs,
+                            n_bpf, st);
   return launch_d<float>(d, PoolJob<float>{nullptr, nullptr, 0, 1, 1, 0},
-                         job<float>(x, blk, BH, n_frames, n_bpf, x_stride, out_stride), frm, BH, tpf, bs, n_bpf, st);
+                         job<float>(x, blk, BH, n_frames, n_bpf, x_stride, out_stride), frm, no_lag(), BH, tpf, bs,
+                         n_bpf, st);
+}
+
+hipError_t launch_pool_step(const PoolStepArgs& a, bool bf16, int d, hipStream_t st) {
+  const LagJob lag{a.k_blk, a.k_frm, a.f_lag, a.n_lag > 0 ? a.n_lag : 1, a.cache_stride, a.BH * a.n_lag * d};
+  float* kb_new = a.k_blk + static_cast<size_t>(a.f_new) * a.n_bpf * d;
+  if (bf16)
+    return launch_d<__bf16>(d, job<__bf16>(a.q, a.q_blk, a.BH, a.n_qframes, a.n_bpf, a.q_stride, a.n_qframes),
+                            job<__bf16>(a.k, kb_new, a.BH, a.n_new, a.n_bpf, a.k_stride, a.cache_stride), nullptr, lag,
+                            a.BH, a.tpf, a.bs, a.n_bpf, st);
+  return launch_d<float>(d, job<float>(a.q, a.q_blk, a.BH, a.n_qframes, a.n_bpf, a.q_stride, a.n_qframes),
+                         job<float>(a.k, kb_new, a.BH, a.n_new, a.n_bpf, a.k_stride, a.cache_stride), nullptr, lag, a.BH,
+                         a.tpf, a.bs, a.n_bpf, st);
 }
 
 // ---------------------------------------------------------------------------------
@@ -268,13 +333,15 @@ struct ProJob {
   float rev[kMaxPairs];           // turn per unit of position of each rotary pair (revolutions)
 };
 
+// One block of one job per workgroup: wave q takes loads u in [q kQuarter, (q + 1) kQuarter)
+// of every batch; part_s holds the quarter sums of waves 1..3.
 template <typename T, int D>
-__global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> p, int tpf, int bs, int n_bpf) {
+__device__ __forceinline__ void prologue_block(const ProJob<T>& p, int w, int tpf, int bs, int n_bpf,
+                                               float (*part_s)[kWave][Chunk16<T>::E]) {
   constexpr int E = Chunk16<T>::E;
   constexpr int C = D / E;
   constexpr int TL = kWave / C;
-  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kPoolWaves + threadIdx.x / kWave);
-  if (w >= p.n_blocks) return;
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave, c = lane % C, s = lane / C;
   const int bf = w / n_bpf, j = w - bf * n_bpf;
   const int bh = bf / p.n_frames, f = bf - bh * p.n_frames;
@@ -297,29 +364,27 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
     rev[m] = p.rev[k];
   }
   const int pos_t = p.frame0 + f;
-  // the lane's first token of each batch: row and column by one division, then the
-  // column advances by TL per token (wrapping into the next row; a row narrower than TL
-  // wraps several times)
-  const int tok0 = j * bs + s;
 
-  float a[E], b[E];
+  float A[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) a[e] = b[e] = 0.f;
-  int row = 0, col = 0;
+  for (int e = 0; e < E; ++e) A[e] = 0.f;
   for (int t0 = 0; t0 < len; t0 += kBatch * TL) {
-    uint4 v[kBatch];
+    uint4 v[kQuarter];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int t = t0 + s + u * TL;
+    for (int u = 0; u < kQuarter; ++u) {
+      const int t = t0 + s + (q * kQuarter + u) * TL;
       v[u] = t < len ? *reinterpret_cast<const uint4*>(xin + static_cast<size_t>(t) * D) : make_uint4(0, 0, 0, 0);
     }
+    // the lane's first token of this quarter: row and column by one division, then the
+    // column advances by TL per token (wrapping into the next row; a row narrower than TL
+    // wraps several times)
+    const int tok = j * bs + t0 + s + q * kQuarter * TL;
+    int row = tok / p.lat_w;
+    int col = tok - row * p.lat_w;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int t = t0 + s + u * TL;
-      if (u == 0) {
-        row = (tok0 + t0) / p.lat_w;
-        col = (tok0 + t0) - row * p.lat_w;
-      } else {
+    for (int u = 0; u < kQuarter; ++u) {
+      const int t = t0 + s + (q * kQuarter + u) * TL;
+      if (u > 0) {
         col += TL;
         while (col >= p.lat_w) {
           col -= p.lat_w;
@@ -354,12 +419,26 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
       const bool valid = t < len;
       if (valid) Out16<T>::store(yout + static_cast<size_t>(t) * D, o);
 #pragma unroll
-      for (int e = 0; e < E; ++e) ((u & 1) ? b : a)[e] += valid ? o[e] : 0.f;
+      for (int e = 0; e < E; ++e) A[e] += valid ? o[e] : 0.f;
     }
   }
-  float sum[E];
+  // the block mean from the four quarter sums, in the order lf_pool uses
+  if (q > 0) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) sum[e] = token_lane_sum<C>(a[e] + b[e]);
+    for (int e = 0; e < E; ++e) part_s[q - 1][lane][e] = A[e];
+  }
+  __syncthreads();
+  if (q != 0) return;
+  float Aq[kQuarters][E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    Aq[0][e] = A[e];
+    Aq[1][e] = part_s[0][lane][e];
+    Aq[2][e] = part_s[1][lane][e];
+    Aq[3][e] = part_s[2][lane][e];
+  }
+  float sum[E];
+  combine_quarters<E, C>(Aq, sum);
   if (lane < C) {
     const float invl = 1.0f / static_cast<float>(len);
     float* out = p.blk + ((static_cast<size_t>(bh) * p.out_stride + f) * n_bpf + j) * D + lane * E;
@@ -371,12 +450,32 @@ __global__ void __launch_bounds__(kPoolWaves * kWave) prologue_kernel(ProJob<T> 
 }
 
 template <typename T, int D>
-static hipError_t launch_prologue_t(const ProlArgs& a, hipStream_t st) {
-  ProJob<T> p{static_cast<const T*>(a.x), static_cast<T*>(a.y), a.gamma, a.blk, a.x_stride, a.y_stride, a.n_frames, a.frame0,
-              a.out_stride, a.BH * a.n_frames * a.n_bpf, a.lat_w, a.eps, {}};
+__global__ void __launch_bounds__(kQuarters * kWave) prologue_kernel(ProJob<T> jq, ProJob<T> jk, LagJob lag, int nq_wgs,
+                                                                     int nk_wgs, int tpf, int bs, int n_bpf) {
+  __shared__ float part_s[kQuarters - 1][kWave][Chunk16<T>::E];
+  const int w = blockIdx.x;
+  if (w < nq_wgs)
+    prologue_block<T, D>(jq, w, tpf, bs, n_bpf, part_s);
+  else if (w < nq_wgs + nk_wgs)
+    prologue_block<T, D>(jk, w - nq_wgs, tpf, bs, n_bpf, part_s);
+  else
+    lag_item<D>(lag, (w - nq_wgs - nk_wgs) * (kQuarters * kWave) + threadIdx.x, tpf, bs, n_bpf);
+}
+
+template <typename T, int D>
+static ProJob<T> pro_job(const ProlArgs& a, const void* x, void* y, const float* gamma, float* blk, long long x_stride,
+                         long long y_stride, int out_stride) {
+  ProJob<T> p{static_cast<const T*>(x), static_cast<T*>(y), gamma, blk, x_stride, y_stride, a.n_frames, a.frame0,
+              out_stride, a.BH * a.n_frames * a.n_bpf, a.lat_w, a.eps, {}};
   for (int k = 0; k < D / 2; ++k) p.rev[k] = a.rev[k];
-  const unsigned grid = static_cast<unsigned>((p.n_blocks + kPoolWaves - 1) / kPoolWaves);
-  hipLaunchKernelGGL((prologue_kernel<T, D>), dim3(grid), dim3(kPoolWaves * kWave), 0, st, p, a.tpf, a.bs, a.n_bpf);
+  return p;
+}
+
+template <typename T, int D>
+static hipError_t launch_prologue_t(const ProlArgs& a, hipStream_t st) {
+  const ProJob<T> p = pro_job<T, D>(a, a.x, a.y, a.gamma, a.blk, a.x_stride, a.y_stride, a.out_stride);
+  hipLaunchKernelGGL((prologue_kernel<T, D>), dim3(static_cast<unsigned>(p.n_blocks)), dim3(kQuarters * kWave), 0, st, p,
+                     p, no_lag(), p.n_blocks, 0, a.tpf, a.bs, a.n_bpf);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (a.frm == nullptr) return hipSuccess;
   const int n_sf = a.BH * a.n_frames;
@@ -389,6 +488,27 @@ static hipError_t launch_prologue_t(const ProlArgs& a, hipStream_t st) {
 hipError_t launch_prologue(const ProlArgs& a, bool bf16, int d, hipStream_t st) {
   if (bf16) return d == 128 ? launch_prologue_t<__bf16, 128>(a, st) : launch_prologue_t<__bf16, 64>(a, st);
   return d == 128 ? launch_prologue_t<float, 128>(a, st) : launch_prologue_t<float, 64>(a, st);
+}
+
+// Queries and the chunk's new keys in one launch (a.x/a.y/a.gamma/a.blk: the queries;
+// the step arguments: the keys, written into a KV cache view, their block means into a
+// pooled-key cache at frame f_new), plus the lagged frame means.
+template <typename T, int D>
+static hipError_t launch_prologue_step_t(const ProlArgs& a, const ProlStepArgs& s, hipStream_t st) {
+  const ProJob<T> jq = pro_job<T, D>(a, a.x, a.y, a.gamma, a.blk, a.x_stride, a.x_stride, a.n_frames);
+  const ProJob<T> jk = pro_job<T, D>(a, s.k, s.k_out, s.gamma_k, s.k_blk + static_cast<size_t>(s.f_new) * a.n_bpf * D,
+                                     a.x_stride, s.k_out_stride, s.cache_stride);
+  const LagJob lag{s.k_blk, s.k_frm, s.f_lag, s.n_lag > 0 ? s.n_lag : 1, s.cache_stride, a.BH * s.n_lag * D};
+  const unsigned grid = static_cast<unsigned>(jq.n_blocks + jk.n_blocks) + lag_wgs<D>(lag);
+  hipLaunchKernelGGL((prologue_kernel<T, D>), dim3(grid), dim3(kQuarters * kWave), 0, st, jq, jk, lag, jq.n_blocks,
+                     jk.n_blocks, a.tpf, a.bs, a.n_bpf);
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue_step(const ProlArgs& a, const ProlStepArgs& s, bool bf16, int d, hipStream_t st) {
+  if (bf16)
+    return d == 128 ? launch_prologue_step_t<__bf16, 128>(a, s, st) : launch_prologue_step_t<__bf16, 64>(a, s, st);
+  return d == 128 ? launch_prologue_step_t<float, 128>(a, s, st) : launch_prologue_step_t<float, 64>(a, s, st);
 }
 
 }  // namespace lf

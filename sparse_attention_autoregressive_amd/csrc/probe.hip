@@ -1,5 +1,6 @@
-// Dense bf16 matrix-core ceiling: register-only MFMA chains, no memory traffic inside the
-// loop, plus the shader clock over the loop measured against the 100 MHz reference.
+// Measurement aids: the dense bf16 matrix-core ceiling (register-only MFMA chains, no
+// memory traffic inside the loop, plus the shader clock over the loop measured against
+// the 100 MHz reference) and the achievable HBM read rate (a plain streaming read).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -43,6 +44,35 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(float* __restrict__ sin
 
 hipError_t launch_mfma_probe(int n_wg, int iters, float* sink, long long* clocks, hipStream_t st) {
   hipLaunchKernelGGL(mfma_probe_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(256), 0, st, sink, clocks, iters);
+  return hipGetLastError();
+}
+
+// Streaming read: every thread reads 16-byte chunks i, i + stride, ... of the buffer with
+// eight loads in flight and folds them into one float (so the loads are kept).
+constexpr int kReadThreads = 256;
+__global__ void __launch_bounds__(kReadThreads) hbm_read_kernel(const uint4* __restrict__ x, long long n16,
+                                                                float* __restrict__ sink) {
+  const long long tid = static_cast<long long>(blockIdx.x) * kReadThreads + threadIdx.x;
+  const long long stride = static_cast<long long>(gridDim.x) * kReadThreads;
+  uint32_t acc = 0;
+  long long i = tid;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = x[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = x[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[tid] = __uint_as_float(acc);
+}
+
+hipError_t launch_hbm_read(const void* x, long long bytes, int n_wg, float* sink, hipStream_t st) {
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(kReadThreads), 0, st,
+                     static_cast<const uint4*>(x), bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -10,7 +10,10 @@ per-layer sweep) allocate nothing.
 Steady state (`PooledKeyCache`): a frame's keys do not change once the frame is in the
 KV cache, so their block and frame means are computed once and kept; each later call
 pools only the chunk's queries and its own key frames, and selection reads the cached
-prefix. Results are bitwise those of the uncached path, since every frame's means are
+prefix. The chunk's own frames are always kept, so their frame means are first read by
+the next chunk: each steady-state pooling launch forms the frame means of the previous
+chunk's frames ("lagged") instead of its own, and `complete_cache` adds the last
+chunk's. Results are bitwise those of the uncached path, since every frame's means are
 computed by the same code from the same tokens.
 """
 from __future__ import annotations
@@ -20,8 +23,8 @@ from typing import List, Sequence
 
 import torch
 
-from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_pool_qk, lf_select, lf_select_blocks,
-               lf_select_blocks_1d, lf_select_frames, lf_sparse_attn, n_bpf)
+from . import (Geom, lf_block_budget, lf_cag_schedule, lf_pool, lf_pool_qk, lf_pool_step, lf_select,
+               lf_select_blocks, lf_select_blocks_1d, lf_select_frames, lf_sparse_attn, n_bpf)
 
 
 @dataclass
@@ -153,21 +156,36 @@ def new_frames(p: ChunkPlan) -> int:
     return p.n_kframes - p.n_qframes
 
 
+def _lag(p: ChunkPlan):
+    """The previous chunk's frames: (first frame, count) of the lagged frame means."""
+    f0 = new_frames(p)
+    n = min(p.n_qframes, f0)
+    return f0 - n, n
+
+
 def pool_cached(ws: Workspace, cache: PooledKeyCache, q: torch.Tensor, k: torch.Tensor):
     """Pools the chunk's queries and only its own key frames (the last n_qframes of the
-    key prefix k) into `cache`, in one launch."""
+    key prefix k) into `cache`, plus the frame means of the previous chunk's frames from
+    their cached block means, in one launch."""
     p = ws.plan
     f0, tpf = new_frames(p), p.geom.tokens_per_frame
-    lf_pool_qk(q, k[:, :, f0 * tpf:], p.geom, p.n_qframes, p.n_qframes, ws.q_blk,
-               cache.blk(f0, p.n_kframes), cache.frm(f0, p.n_kframes))
+    fl, nl = _lag(p)
+    lf_pool_step(q, k[:, :, f0 * tpf:], p.geom, p.n_qframes, p.n_qframes, f0, fl, nl, ws.q_blk, cache.k_blk,
+                 cache.k_frm)
 
 
 def pool_keys_cached(p: ChunkPlan, cache: PooledKeyCache, k: torch.Tensor):
     """Pools only the chunk's own key frames into `cache` (a dense chunk needs no pooled
-    queries, but later chunks select over its keys)."""
+    queries, but later chunks select over its keys), with the lagged frame means."""
     f0, tpf = new_frames(p), p.geom.tokens_per_frame
-    lf_pool(k[:, :, f0 * tpf:], p.geom, p.n_qframes, blk_out=cache.blk(f0, p.n_kframes),
-            frm_out=cache.frm(f0, p.n_kframes))
+    fl, nl = _lag(p)
+    lf_pool_step(None, k[:, :, f0 * tpf:], p.geom, 0, p.n_qframes, f0, fl, nl, None, cache.k_blk, cache.k_frm)
+
+
+def complete_cache(p: ChunkPlan, cache: PooledKeyCache):
+    """The frame means of chunk p's own frames (which its pooling leaves to the next
+    chunk), from their cached block means: for a cache no later chunk will extend."""
+    lf_pool_step(None, None, p.geom, 0, 0, 0, new_frames(p), p.n_qframes, None, cache.k_blk, cache.k_frm)
 
 
 def select_cached(ws: Workspace, cache: PooledKeyCache):
@@ -193,8 +211,10 @@ def denoise_steps(ws: Workspace, cache: PooledKeyCache, k_cache: torch.Tensor, v
     step selects over the key prefix k_{:i}, stages 2-3). `steps` yields (q, k_chunk,
     v_chunk, out) per step: the step's queries, the chunk's own keys and values -- copied
     here into the KV caches at the chunk's frames -- and the output. The history's pooled
-    keys in `cache` are read as they are (pooled once, by the earlier chunks); the chunk's
-    own frames are re-pooled at every step, since their keys change. k_cache and v_cache
+    keys in `cache` are read as they are (pooled once, by the earlier chunks; each step
+    re-forms the previous chunk's lagged frame means, the same values); the chunk's own
+    frames' block means are re-pooled at every step, since their keys change, and their
+    frame means are left to the next chunk (or `complete_cache`). k_cache and v_cache
     hold the clip ([B, H, >= n_kframes * tpf, d]); returns the last step's output."""
     p = ws.plan
     tpf = p.geom.tokens_per_frame
@@ -276,14 +296,16 @@ class SweepWorkspace:
 
 
 def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                o: torch.Tensor, mark=None, cache: PooledKeyCache = None) -> torch.Tensor:
+                o: torch.Tensor, mark=None, cache: PooledKeyCache = None, complete: bool = True) -> torch.Tensor:
     """All chunks of one layer in order. q, k, v, o: [B, H, n_frames*tpf, d] holding the
     whole clip; chunk i reads its query frames and the key prefix as views and writes its
     frames of o. Enqueued on the current stream; returns o. `mark(i, stage)`, if given,
     is called before each stage ("pool", "select", "attn") and with stage
     "end" after chunk i (e.g. to record timing events). With a `cache` (this layer's,
     sized for the clip), every chunk pools only its own key frames into it, the dense
-    first chunk included, and selection reads the cached prefix: the same outputs."""
+    first chunk included, and selection reads the cached prefix: the same outputs. The
+    cache then holds every frame's means on return (the last chunk's frame means are
+    formed after its attention, by `complete_cache`), unless `complete` is False."""
     sp = sw.plan
     tpf = sp.geom.tokens_per_frame
     tick = mark if mark is not None else (lambda i, stage: None)
@@ -310,4 +332,6 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
             tick(i, "attn")
             attend(ws, qv, kv, vv, ov)
         tick(i, "end")
+    if cache is not None and complete and sp.chunks:
+        complete_cache(sp.chunks[-1], cache)
     return o

@@ -31,10 +31,10 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert {"lf_pool", "lf_pool_qk", "lf_select_frames", "lf_select_blocks", "lf_select", "lf_sparse_attn",
             "lf_cag_schedule", "lf_block_budget", "lf_last_error", "lf_abi_version",
-            "lf_probe_mfma_bf16"} <= set(names)
+            "lf_probe_mfma_bf16", "lf_probe_hbm_read", "lf_pool_step", "lf_qk_prologue_step"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lf.lf_abi_version() == 3
+    assert lf.lf_abi_version() == 4
 
 
 @pytest.mark.parametrize("n,T,s_base,s_t", [(7, 4, 0.95, 0.8), (7, 4, 0.95, 0.85), (5, 2, 0.9, 0.6),
@@ -254,6 +254,11 @@ def test_probe_validation():
     _err(c.lf_probe_mfma_bf16(4, 0, FAKE, FAKE, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_probe_mfma_bf16(4, 10, FAKE, FAKE + 4, None), lf.LF_ERR_INVALID_ARG)
     _err(c.lf_probe_mfma_bf16(4, 10, None, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_hbm_read(FAKE, 1 << 20, 0, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_hbm_read(FAKE, 1000, 4, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_hbm_read(FAKE, 0, 4, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_hbm_read(FAKE + 8, 1 << 20, 4, FAKE, None), lf.LF_ERR_INVALID_ARG)
+    _err(c.lf_probe_hbm_read(None, 1 << 20, 4, FAKE, None), lf.LF_ERR_INVALID_ARG)
 
 
 def test_select_1d_validation():
@@ -295,3 +300,47 @@ def test_prologue_output_stride_validation():
     F = FAKE
     _err(c.lf_qk_prologue(F, F + 4096, F, 1, lf.Geom(1, 2, 128, 1560, 64, 0, 4679), 3, 0, 52, 1e-6, 1e4, F, None,
                           None), lf.LF_ERR_INVALID_ARG)   # output stride below 3 frames
+
+
+def test_pool_step_validation():
+    c = _c()
+    F = FAKE
+    g = lf.Geom(1, 2, 128, 1560, 64, 0, 0, 24)            # a 24-frame pooled-key cache
+    call = lambda gg=g, q=F, k=F, nq=3, nn=3, fn=18, fl=15, nl=3, qb=F, kb=F, kf=F, dt=1: c.lf_pool_step(
+        q, k, dt, gg, nq, nn, fn, fl, nl, qb, kb, kf, None)
+    _err(call(gg=lf.Geom(1, 2, 128, 1560, 64)), lf.LF_ERR_INVALID_ARG)          # no cache frame count
+    _err(call(fn=22), lf.LF_ERR_INVALID_ARG)                                     # new frames past the cache
+    _err(call(fl=22), lf.LF_ERR_INVALID_ARG)                                     # lagged frames past the cache
+    _err(call(fl=16), lf.LF_ERR_INVALID_ARG)                                     # lagged overlaps new
+    _err(call(nq=-1), lf.LF_ERR_INVALID_ARG)
+    _err(call(nl=-1), lf.LF_ERR_INVALID_ARG)
+    _err(call(q=None), lf.LF_ERR_INVALID_ARG)
+    _err(call(qb=None), lf.LF_ERR_INVALID_ARG)
+    _err(call(k=None), lf.LF_ERR_INVALID_ARG)
+    _err(call(kf=None), lf.LF_ERR_INVALID_ARG)
+    _err(call(kb=F + 4), lf.LF_ERR_INVALID_ARG)
+    _err(call(dt=7), lf.LF_ERR_UNSUPPORTED)
+    _err(call(gg=lf.Geom(1, 2, 128, 1560, 64, 4679, 0, 24)), lf.LF_ERR_INVALID_ARG)    # query stride < 3 frames
+    _err(call(gg=lf.Geom(1, 2, 128, 1560, 64, 0, 4679, 24)), lf.LF_ERR_INVALID_ARG)    # key stride < 3 frames
+    # nothing to do: accepted without touching any pointer
+    assert c.lf_pool_step(None, None, 1, g, 0, 0, 0, 0, 0, None, None, None, None) == lf.LF_OK
+
+
+def test_prologue_step_validation():
+    c = _c()
+    F = FAKE
+    g = lf.Geom(1, 2, 128, 1560, 64, 0, 0, 24)
+    call = lambda gg=g, n=3, f0=18, lw=52, eps=1e-6, th=1e4, x=F, y=F + 4096, fn=18, fl=15, nl=3, kf=F: \
+        c.lf_qk_prologue_step(x, F + 8192, y, F + 12288, F, F, 1, gg, n, f0, lw, eps, th, fn, fl, nl, F, F, kf, None)
+    _err(call(lw=50), lf.LF_ERR_INVALID_ARG)
+    _err(call(eps=0.0), lf.LF_ERR_INVALID_ARG)
+    _err(call(th=1.0), lf.LF_ERR_INVALID_ARG)
+    _err(call(n=0), lf.LF_ERR_INVALID_ARG)
+    _err(call(f0=-1), lf.LF_ERR_INVALID_ARG)
+    _err(call(y=F), lf.LF_ERR_INVALID_ARG)                                       # output aliases input
+    _err(call(fn=22), lf.LF_ERR_INVALID_ARG)
+    _err(call(fl=17), lf.LF_ERR_INVALID_ARG)                                     # lagged overlaps new
+    _err(call(kf=None), lf.LF_ERR_INVALID_ARG)
+    _err(call(gg=lf.Geom(1, 2, 128, 1560, 64)), lf.LF_ERR_INVALID_ARG)
+    _err(call(gg=lf.Geom(1, 2, 96, 1560, 64, 0, 0, 24)), lf.LF_ERR_UNSUPPORTED)
+    _err(call(gg=lf.Geom(1, 2, 128, 1560, 64, 0, 4679, 24)), lf.LF_ERR_INVALID_ARG)

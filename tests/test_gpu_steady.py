@@ -2,7 +2,8 @@
 (480p chunk 7 of 7: 18 history frames, the chunk's 3 frames, 4 steps): the history's keys
 and values sit in a KV cache and their pooled keys in a pooled-key cache filled once; each
 step writes the chunk's new keys and values into the cache, re-pools only the chunk's
-frames and attends over the cached prefix.
+frames' block means (their frame means are first read by the next chunk) and attends over
+the cached prefix.
 
 Every step's pooled queries, lists and output equal the uncached path on that step's
 packed inputs bitwise; the history's cached means never change; the last step's masks
@@ -13,8 +14,8 @@ import torch
 
 import synth
 import sparse_attention_autoregressive_amd as lf
-from sparse_attention_autoregressive_amd.pipeline import (PooledKeyCache, Workspace, denoise_steps, hsa_chunk,
-                                                          new_frames)
+from sparse_attention_autoregressive_amd.pipeline import (PooledKeyCache, Workspace, complete_cache, denoise_steps,
+                                                          hsa_chunk, new_frames)
 from support import compare_attention, compare_masks, lib_k_b, log, plan_of, run_oracle_masks, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +58,9 @@ def test_denoise_steps_chunk7():
     torch.cuda.synchronize()
     assert len(seen) == T and last is outs[-1]
     assert torch.equal(cache.blk(0, f0), hist_blk) and torch.equal(cache.frm(0, f0), hist_frm)
-    assert torch.isnan(cache.k_frm[:, :, w.n_kframes:]).all() and torch.isnan(k_cache[:, :, b:]).all()
+    assert torch.isnan(cache.k_frm[:, :, f0:]).all() and torch.isnan(k_cache[:, :, b:]).all()
+    complete_cache(plan, cache)                             # the chunk's frame means, left to the next chunk
+    torch.cuda.synchronize()
     for t, (q, k, v) in enumerate(dev_steps):
         ref = Workspace(plan, torch.bfloat16, dev)
         hsa_chunk(ref, q, k, v)

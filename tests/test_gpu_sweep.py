@@ -140,8 +140,9 @@ def test_steady_state_chunk_equals_uncached(name):
     KV cache with room for more frames (so the query-side and key-side head strides
     differ), the history's pooled keys in a cache filled beforehand. Pooled queries, the
     cache's new frames, lists and output equal the uncached call on packed tensors
-    bitwise."""
-    from sparse_attention_autoregressive_amd.pipeline import Workspace, hsa_chunk, hsa_chunk_cached, new_frames
+    bitwise; the chunk's own frame means are written by `complete_cache` only."""
+    from sparse_attention_autoregressive_amd.pipeline import (Workspace, complete_cache, hsa_chunk, hsa_chunk_cached,
+                                                              new_frames)
     from support import lib_k_b, plan_of
     w = synth.WORKLOADS[name]
     x = synth.make(w)
@@ -165,7 +166,11 @@ def test_steady_state_chunk_equals_uncached(name):
     hsa_chunk_cached(ws, cache, q, kc[:, :, :w.lk], vc[:, :, :w.lk])
     torch.cuda.synchronize()
     assert torch.equal(ref.q_blk, ws.q_blk)
-    assert torch.equal(ref.k_blk, cache.blk(0, w.n_kframes)) and torch.equal(ref.k_frm, cache.frm(0, w.n_kframes))
-    assert torch.isnan(cache.k_frm[:, :, w.n_kframes:]).all()
+    assert torch.equal(ref.k_blk, cache.blk(0, w.n_kframes)) and torch.equal(ref.k_frm[:, :, :f0], cache.frm(0, f0))
+    assert torch.isnan(cache.k_frm[:, :, f0:]).all(), "the chunk's own frame means are left to the next chunk"
     assert torch.equal(ref.frames, ws.frames) and torch.equal(ref.blocks, ws.blocks)
     assert torch.equal(ref.o, ws.o)
+    complete_cache(plan, cache)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.k_frm, cache.frm(0, w.n_kframes))
+    assert torch.isnan(cache.k_frm[:, :, w.n_kframes:]).all() and torch.isnan(cache.k_blk[:, :, ref.k_blk.shape[2]:]).all()
