@@ -44,16 +44,31 @@ def _short(name: str) -> str:
 
 
 def trace(db: str, title: str, cmd: str) -> str:
-    rows = sqlite3.connect(db).execute("select name, duration from kernels").fetchall()
+    """Per-kernel table; a kernel launched with several grid sizes (e.g. pooling a whole
+    key prefix and pooling one chunk's frames) gets one row per grid size."""
+    c = sqlite3.connect(db)
+    try:
+        rows = c.execute("select name, duration, grid_x / workgroup_x from kernels").fetchall()
+        with_grid = True
+    except sqlite3.OperationalError:                    # a database without launch shapes
+        rows = [(n, d, None) for n, d in c.execute("select name, duration from kernels").fetchall()]
+        with_grid = False
     by = {}
-    for n, d in rows:
-        by.setdefault(n, []).append(d / 1000.0)
-    out = [f"# {title}", "", f"Command: `{cmd}`", "",
-           "| kernel | calls | mean us | median us | min us |", "|---|---|---|---|---|"]
-    for n, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+    for n, d, wgs in rows:
+        by.setdefault((n, wgs), []).append(d / 1000.0)
+    grids = {}
+    for n, wgs in by:
+        grids.setdefault(n, set()).add(wgs)
+    out = [f"# {title}", "", f"Command: `{cmd}`", ""]
+    if with_grid:
+        out += ["| kernel | workgroups | calls | mean us | median us | min us |", "|---|---|---|---|---|---|"]
+    else:
+        out += ["| kernel | calls | mean us | median us | min us |", "|---|---|---|---|---|"]
+    for (n, wgs), ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         if "lf::" not in n and "_ZN2lf" not in n:
             continue
-        out.append(f"| `{_short(n)}` | {len(ds)} | {statistics.mean(ds):.2f} | "
+        grid = f" {wgs} |" if with_grid else ""
+        out.append(f"| `{_short(n)}` |{grid} {len(ds)} | {statistics.mean(ds):.2f} | "
                    f"{statistics.median(ds):.2f} | {min(ds):.2f} |")
     return "\n".join(out)
 

@@ -29,6 +29,19 @@ def test_trace_lists_only_library_kernels(tmp_path):
     assert "copy_kernel" not in out
 
 
+def test_trace_splits_launch_shapes(tmp_path):
+    c = sqlite3.connect(str(tmp_path / "g.db"))
+    c.execute("create table kernels (name text, duration integer, grid_x integer, workgroup_x integer)")
+    c.executemany("insert into kernels values (?, ?, ?, ?)",
+                  [("lf::block_mean_kernel", 20_000, 256 * 900, 256), ("lf::block_mean_kernel", 22_000, 256 * 900, 256),
+                   ("lf::block_mean_kernel", 6_000, 256 * 150, 256)])
+    c.commit()
+    c.close()
+    out = profsum.trace(str(tmp_path / "g.db"), "T", "cmd")
+    assert "| `lf::block_mean_kernel` | 900 | 2 | 21.00 | 21.00 | 20.00 |" in out
+    assert "| `lf::block_mean_kernel` | 150 | 1 | 6.00 | 6.00 | 6.00 |" in out
+
+
 def test_traffic_scales_each_counter_by_the_copy(tmp_path):
     # a 1 MiB calibration copy whose reads the counter reports twice over and whose
     # writes it reports exactly; the kernel's per-dispatch values are corrected alike
