@@ -290,8 +290,10 @@ def blas_threads():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 500; 20 sweeps for the sweep workload)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 200, enough for the clocks to settle; 3 sweeps)")
     ap.add_argument("--workload", default="480p_chunk7of7", choices=sorted(synth.WORKLOADS) + [synth.SWEEP.name])
     ap.add_argument("--layers", type=int, default=0,
                     help="independent input sets cycled per step (0: enough to exceed 512 MB)")
@@ -308,6 +310,11 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sweep = args.workload == synth.SWEEP.name
+    if args.steps is None:
+        args.steps = 20 if sweep else 500
+    if args.warmup is None:
+        args.warmup = 3 if sweep else 200
     if args.workload == synth.SWEEP.name:
         return bench_sweep(args)
     dev = torch.device("cuda")
@@ -355,7 +362,7 @@ def main():
     for c, (_, k, _) in zip(caches, sets):
         lf.lf_pool(k[:, :, :f0 * w.tpf], g, f0, blk_out=c.blk(0, f0), frm_out=c.frm(0, f0))
 
-    def step(i, ev=None, cached=False):
+    def step(i, ev=None, cached=False, upto=3):
         lf.lf_cag_schedule(w.n_chunks, w.T, w.s_base, w.s_target, chunk_flops(w))
         ws = wss[i % len(sets)]
         q, k, v = sets[i % len(sets)]
@@ -364,6 +371,7 @@ def main():
             calls = [lambda: pool_cached(ws, c, q, k), lambda: select_cached(ws, c), lambda: attend(ws, q, k, v)]
         else:
             calls = [lambda: pool(ws, q, k), lambda: select(ws), lambda: attend(ws, q, k, v)]
+        calls = calls[:upto]
         for j, c_ in enumerate(calls):
             if ev is not None:
                 ev[j].record(stream)
@@ -386,17 +394,41 @@ def main():
         wall = time.perf_counter() - t0
         # per-call times: the same steps again with events between calls, all enqueued while
         # a spin kernel holds the stream, so host launch gaps do not show up as kernel time
-        evs = [[TimingEvent() for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+        n_ev = min(args.steps, 100)
+        evs = [[TimingEvent() for _ in range(len(KERNELS) + 1)] for _ in range(n_ev)]
         hold_stream()
-        for i in range(args.steps):
+        for i in range(n_ev):
             step(i, evs[i], cached=cached)
         torch.cuda.synchronize()
         per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(KERNELS))]
-                        for i in range(args.steps)]) * 1e3                      # us
+                        for i in range(n_ev)]) * 1e3                      # us
         return wall * 1e3 / args.steps, per.mean(axis=0), np.median(per, axis=0), np.percentile(per, [10, 90], axis=0)
+
+    def stage_times_in_loop(n, cached=False):
+        """Each stage's mean time inside the step loop: n steps timed by HIP events around
+        the whole loop on the launch stream (queued behind a spin kernel, so host launch
+        gaps do not count) with the first 1, 2 and 3 stages, differenced. Consecutive
+        kernels of a step run back to back, so each difference is that stage's launches'
+        own time; event pairs around single launches add each marker's dispatch gap (about
+        5 us) to every interval. Returns (per-stage us, full-step us)."""
+        per = []
+        for upto in (1, 2, 3):
+            torch.cuda.synchronize()
+            hold_stream(max(50.0, 0.25 * n))
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record(stream)
+            for i in range(n):
+                step(i, cached=cached, upto=upto)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / n)
+        return np.array([per[0], per[1] - per[0], per[2] - per[1]]), per[2]
 
     ms_per_step, mean_us, med_us, pct_us = timed(False)
     ss_ms, ss_mean, ss_med, _ = timed(True)
+    loop_us, loop_step_us = stage_times_in_loop(args.steps)
+    ss_loop_us, ss_loop_step_us = stage_times_in_loop(args.steps, cached=True)
+    attn_loop_us = float(loop_us[2])
     state = gpu_state_under_load(lambda i: step(i)) if not args.no_extras else None
 
     extras = not args.no_extras
@@ -406,31 +438,34 @@ def main():
     hbm = hbm_ceiling() if extras else None
     blocks = wss[0].blocks.cpu().numpy()
     f_dense, f_active = flops_of(w, blocks)
-    t_attn = mean_us[2] * 1e-6
-    t_path = mean_us.sum() * 1e-6
-    attn_tflops = f_active / t_attn / 1e12
+    # active FLOPs per attention launch of the loop (the input sets' lists differ slightly)
+    f_sets = [flops_of(w, ws.blocks.cpu().numpy())[1] for ws in wss]
+    f_active_loop = float(np.mean([f_sets[i % len(sets)] for i in range(args.steps)]))
+    t_attn = attn_loop_us * 1e-6
+    t_path = loop_step_us * 1e-6
+    attn_tflops = f_active_loop / t_attn / 1e12
     value = f_dense / (ms_per_step * 1e-3) / 1e12
-    sel_pct = 100.0 * mean_us[1] / mean_us[2]
+    sel_pct = 100.0 * loop_us[1] / loop_us[2]
     pool_gbs = {"pool": (pool_bytes(w, w.n_qframes, False) + pool_bytes(w, w.n_kframes, True))
-                        / (mean_us[0] * 1e-6) / 1e9}
+                        / (loop_us[0] * 1e-6) / 1e9}
     n_rows = w.B * w.H * plan.n_qb
     # algorithmic HBM bytes of the selection launch: q~ rows, each head's frame means and
     # block means once (they stay in L2 across the head's rows), T_r and list writes
     sel_bytes = (n_rows * (w.d * 4 + plan.W_f * 4 + plan.W_b * 4)
                  + w.B * w.H * w.n_kframes * (nb + 1) * w.d * 4)
-    sel_gbs = {"select": sel_bytes / (mean_us[1] * 1e-6) / 1e9}
+    sel_gbs = {"select": sel_bytes / (loop_us[1] * 1e-6) / 1e9}
     steady = {
         "what": (f"history pooled keys ({f0} frames) from a per-layer cache filled before timing; a step pools "
                  f"the queries and the chunk's own {w.n_kframes - f0} key frames (block means) with the "
                  f"previous chunk's {n_lag} frame means in one launch, selects over the cache and attends"),
         "value": f_dense / (ss_ms * 1e-3) / 1e12,
         "ms_per_step": ss_ms,
-        "kernel_us_mean": dict(zip(KERNELS, [round(float(x), 2) for x in ss_mean])),
-        "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in ss_med])),
-        "pool_select_pct_of_attn": 100.0 * ss_mean[:2].sum() / ss_mean[2],
-        "dense_equiv_tflops_kernel_sum": f_dense / (ss_mean.sum() * 1e-6) / 1e12,
+        "kernel_us_in_loop": dict(zip(KERNELS, [round(float(x), 2) for x in ss_loop_us])),
+        "kernel_us_event_pairs_mean": dict(zip(KERNELS, [round(float(x), 2) for x in ss_mean])),
+        "pool_select_pct_of_attn": 100.0 * ss_loop_us[:2].sum() / ss_loop_us[2],
+        "dense_equiv_tflops_kernel_sum": f_dense / (ss_loop_step_us * 1e-6) / 1e12,
         "pool_gbs": round((pool_bytes(w, w.n_qframes, False) + pool_bytes(w, w.n_kframes - f0, False)
-                           + lag_bytes(w, n_lag)) / (ss_mean[0] * 1e-6) / 1e9, 1),
+                           + lag_bytes(w, n_lag)) / (ss_loop_us[0] * 1e-6) / 1e9, 1),
     }
 
     cpu = None
@@ -463,14 +498,16 @@ def main():
                    "cag_beta": beta, "input_sets": len(sets)},
         "mfma_pct_peak_active": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
         "select_overhead_pct": sel_pct,
-        "pool_select_pct_of_attn": 100.0 * (mean_us[:2].sum()) / mean_us[2],
+        "pool_select_pct_of_attn": 100.0 * (loop_us[:2].sum()) / loop_us[2],
         "dense_equiv_tflops_attn_only": f_dense / t_attn / 1e12,
         "dense_equiv_tflops_kernel_sum": f_dense / t_path / 1e12,
         "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
-        "kernel_us_mean": dict(zip(KERNELS, [round(float(x), 2) for x in mean_us])),
-        "kernel_us_median": dict(zip(KERNELS, [round(float(x), 2) for x in med_us])),
-        "kernel_us_p10_p90": {k: [round(float(pct_us[0][i]), 2), round(float(pct_us[1][i]), 2)]
-                              for i, k in enumerate(KERNELS)},
+        "kernel_us_in_loop": dict(zip(KERNELS, [round(float(x), 2) for x in loop_us])),
+        "kernel_us_in_loop_what": (f"{args.steps} steps with the first 1, 2, 3 stages, HIP events around each "
+                                   f"loop on the launch stream, differenced"),
+        "kernel_us_event_pairs_mean": dict(zip(KERNELS, [round(float(x), 2) for x in mean_us])),
+        "kernel_us_event_pairs_p10_p90": {k: [round(float(pct_us[0][i]), 2), round(float(pct_us[1][i]), 2)]
+                                          for i, k in enumerate(KERNELS)},
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
         "hbm_ceiling": ({**hbm, "pool_frac": round(pool_gbs["pool"] / hbm["gbs"], 3),
                          "steady_pool_frac": round(steady["pool_gbs"] / hbm["gbs"], 3),
@@ -482,7 +519,10 @@ def main():
         "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_of(w.name)},
+                     "traffic": traffic_of(w.name),
+                     "launch_us": round(attn_loop_us, 2), "active_flops_per_launch": f_active_loop,
+                     "timing": (f"{args.steps} steps timed by HIP events around the loop on the launch "
+                                f"stream, with and without the attention launch (difference)")},
         "mfma_ceiling": ({**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]} if ceiling else None),
         "gpu_state": state,
         "cpu_baseline": cpu,
