@@ -196,25 +196,31 @@ def mfma_ceiling(n_wg: int = 512, iters: int = 20000, reps: int = 3):
             "what": f"register-only v_mfma_f32_32x32x16_bf16 chains, {n_wg} x 4 waves, {iters} x 4 MFMAs per wave"}
 
 
-def hbm_ceiling(gib: int = 2, reps: int = 5):
+def hbm_ceiling(gib: int = 2, reps: int = 3):
     """Measured HBM read rate: a plain streaming read of a `gib` GiB buffer (8x the 256 MB
-    Infinity Cache, so it streams from HBM), best of `reps` launches."""
+    Infinity Cache, so it streams from HBM) at several launch sizes, best launch of each,
+    best size reported."""
     dev = torch.device("cuda")
     x = torch.ones((gib << 30) // 4, dtype=torch.float32, device=dev)
-    n_wg = 256 * 8
-    sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
-    best = 0.0
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        lf.lf_probe_hbm_read(x, n_wg, sink)
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    sizes = (2048, 4096, 8192, 16384)
+    sink = torch.empty(max(sizes) * 256, dtype=torch.float32, device=dev)
+    by_size = {}
+    for n_wg in sizes:
+        best = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lf.lf_probe_hbm_read(x, n_wg, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        by_size[n_wg] = round(best, 1)
     del x
     torch.cuda.empty_cache()
-    return {"gbs": round(best, 1), "what": f"plain streaming read of {gib} GiB, {n_wg} x 256 threads, "
-                                           f"16-byte loads, best of {reps}"}
+    n_best = max(by_size, key=by_size.get)
+    return {"gbs": by_size[n_best], "by_workgroups": by_size,
+            "what": f"plain streaming read of {gib} GiB, 256-thread workgroups, 16-byte loads, best of {reps} "
+                    f"per launch size"}
 
 
 def cpu_model() -> str:

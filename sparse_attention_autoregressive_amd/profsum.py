@@ -15,8 +15,9 @@
     python -m sparse_attention_autoregressive_amd.profsum counters CSV [CSV ...] \
         --title T --cmd C [--sets S ...]
         mean per-dispatch value of every counter in the --pmc runs' counter_collection
-        CSV files (one run per counter set), for each library kernel, and the wave-cycle
-        split of the attention kernel; C is the command with <set> for the counter list.
+        CSV files (one run per counter set), for each library kernel, the wave-cycle
+        split of the attention kernel and each kernel's L2 hit rate (when TCC_HIT_sum and
+        TCC_MISS_sum were collected); C is the command with <set> for the counter list.
 """
 from __future__ import annotations
 
@@ -56,9 +57,6 @@ def trace(db: str, title: str, cmd: str) -> str:
     by = {}
     for n, d, wgs in rows:
         by.setdefault((n, wgs), []).append(d / 1000.0)
-    grids = {}
-    for n, wgs in by:
-        grids.setdefault(n, set()).add(wgs)
     out = [f"# {title}", "", f"Command: `{cmd}`", ""]
     if with_grid:
         out += ["| kernel | workgroups | calls | mean us | median us | min us |", "|---|---|---|---|---|---|"]
@@ -166,6 +164,13 @@ def counters(csvs, title: str, cmd: str, asked=None) -> str:
                         ("SQ_ACTIVE_INST_VMEM", "issuing vector memory"), ("SQ_WAIT_INST_LDS", "waiting on LDS issue")):
             if c in a:
                 out.append(f"- {what} ({c}): {statistics.mean(a[c]) / w * 100:.1f}%")
+    hits = [(label, vals[label]) for _, label in _KERNELS
+            if label in vals and "TCC_HIT_sum" in vals[label] and "TCC_MISS_sum" in vals[label]]
+    if hits:
+        out += ["", "L2 hit rate (TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)):", ""]
+        for label, m in hits:
+            h, s = statistics.mean(m["TCC_HIT_sum"]), statistics.mean(m["TCC_MISS_sum"])
+            out.append(f"- {label}: {h / (h + s) * 100:.1f}% of {h + s:.4g} requests")
     return "\n".join(out)
 
 

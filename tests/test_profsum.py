@@ -94,3 +94,10 @@ def test_counters_means_per_kernel_and_wave_cycle_split(tmp_path):
     assert "attention dispatch duration under counters: median 150.0 us" in out
     assert "- waiting on s_waitcnt (SQ_WAIT_ANY): 25.0%" in out
     assert "- issuing (SQ_ACTIVE_INST_ANY): 40.0%" in out
+
+
+def test_counters_l2_hit_rate(tmp_path):
+    attn = "void lf::attn_bf16_kernel<128>(lf::AttnArgs)"
+    p = _csv(tmp_path / "c.csv", [(1, attn, "TCC_HIT_sum", 75.0, 0, 150_000), (1, attn, "TCC_MISS_sum", 25.0, 0, 150_000)])
+    out = profsum.counters([p], "T", "x <set>")
+    assert "- attention: 75.0% of 100 requests" in out
