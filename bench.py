@@ -215,12 +215,24 @@ def hbm_ceiling(gib: int = 2, reps: int = 3):
             torch.cuda.synchronize()
             best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
         by_size[n_wg] = round(best, 1)
-    del x
+    # read + write: a plain device copy of half the buffer (torch's copy kernel), both
+    # directions' bytes counted -- the ceiling for kernels that write as much as they read
+    half = x.numel() // 2
+    src_, dst_ = x[:half], x[half:2 * half]
+    copy_best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst_.copy_(src_)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_best = max(copy_best, 2 * half * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x, src_, dst_
     torch.cuda.empty_cache()
     n_best = max(by_size, key=by_size.get)
-    return {"gbs": by_size[n_best], "by_workgroups": by_size,
+    return {"gbs": by_size[n_best], "by_workgroups": by_size, "copy_gbs": round(copy_best, 1),
             "what": f"plain streaming read of {gib} GiB, 256-thread workgroups, 16-byte loads, best of {reps} "
-                    f"per launch size"}
+                    f"per launch size; copy_gbs: a device copy of {gib / 2:g} GiB, read and written bytes counted"}
 
 
 def cpu_model() -> str:
@@ -517,7 +529,9 @@ def main():
         "hbm_gbs": {**{k: round(v, 1) for k, v in pool_gbs.items()}, **{k: round(v, 1) for k, v in sel_gbs.items()}},
         "hbm_ceiling": ({**hbm, "pool_frac": round(pool_gbs["pool"] / hbm["gbs"], 3),
                          "steady_pool_frac": round(steady["pool_gbs"] / hbm["gbs"], 3),
-                         "prologue_frac": (round(prologue["hbm_gbs"] / hbm["gbs"], 3) if prologue else None)}
+                         "prologue_frac": (round(prologue["hbm_gbs"] / hbm["gbs"], 3) if prologue else None),
+                         "prologue_frac_of_copy": (round(prologue["hbm_gbs"] / hbm["copy_gbs"], 3)
+                                                   if prologue else None)}
                         if hbm else None),
         "steady_state": steady,
         "one_level": one_level,
