@@ -234,7 +234,10 @@ lf_status lf_qk_prologue_step(const void* q, const void* k_new, void* q_out, voi
  *   [0, n_kframes), no duplicates, the two sets disjoint; W_f (below) must be >= 1.
  * frames_out: [B, H, n_qb, W_f] int32, W_f = n_forced + min(k_f, n_mem), each row
  *   ascending.
- * Limits: d in {64, 128}; n_kframes <= 256; k_f >= 0.
+ * Limits: d in {64, 128}; n_kframes <= 4096 (about 16 minutes of 480p latent frames);
+ *   k_f >= 0. Up to 256 key frames the frame stage ranks by counting (one frame of M per
+ *   thread); beyond, it takes the k_f best in k_f rounds of a workgroup-wide maximum, with
+ *   the same result.
  * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED (d, n_kframes), LF_ERR_HIP.
  * ------------------------------------------------------------------------------- */
 lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
@@ -269,7 +272,7 @@ lf_status lf_select_blocks(const float* q_blk, const float* k_blk, lf_geom g, in
  *   n_forced + min(k_f, n_mem). k_b: as for lf_select_blocks.
  * frames_out: [B, H, n_qb, W_f] int32, or NULL to skip writing T_r.
  * blocks_out: [B, H, n_qb, W_f*min(k_b, n_bpf)] int32.
- * Limits: those of both calls (n_kframes <= 256, n_bpf <= 64).
+ * Limits: those of both calls (n_kframes <= 4096, n_bpf <= 64).
  * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED, LF_ERR_HIP.
  * ------------------------------------------------------------------------------- */
 lf_status lf_select(const float* q_blk, const float* k_frm, const float* k_blk, lf_geom g,

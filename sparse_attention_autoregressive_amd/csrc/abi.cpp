@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 
 #include "../../include/lf.h"
 #include "../../include/lf_probe.h"
@@ -79,12 +80,15 @@ lf_status check_frame_stage(const float* q_blk, const float* k_frm, lf_geom g, i
   if (!aligned16(q_blk) || !aligned16(k_frm)) return fail(LF_ERR_INVALID_ARG, "%s: misaligned buffer", fn);
   bool seen[lf::kMaxFrames] = {};
   bool in_mem[lf::kMaxFrames] = {};
+  std::memset(&a.masks, 0, sizeof(a.masks));
+  const bool listed = n_kframes <= lf::kListFrames;
   for (int i = 0; i < n_mem; ++i) {
     const int f = mem[i];
     if (f < 0 || f >= n_kframes) return fail(LF_ERR_INVALID_ARG, "%s: mem[%d]=%d out of range", fn, i, f);
     if (seen[f]) return fail(LF_ERR_INVALID_ARG, "%s: duplicate memory frame %d", fn, f);
     seen[f] = in_mem[f] = true;
-    a.lists.mem[i] = static_cast<int16_t>(f);
+    if (listed) a.lists.mem[i] = static_cast<int16_t>(f);
+    a.masks.mem[f / 64] |= 1ull << (f % 64);
   }
   for (int i = 0; i < n_forced; ++i) {
     const int f = forced[i];
@@ -92,7 +96,8 @@ lf_status check_frame_stage(const float* q_blk, const float* k_frm, lf_geom g, i
     if (in_mem[f]) return fail(LF_ERR_INVALID_ARG, "%s: frame %d is both forced and in the memory set", fn, f);
     if (seen[f]) return fail(LF_ERR_INVALID_ARG, "%s: duplicate forced frame %d", fn, f);
     seen[f] = true;
-    a.lists.forced[i] = static_cast<int16_t>(f);
+    if (listed) a.lists.forced[i] = static_cast<int16_t>(f);
+    a.masks.forced[f / 64] |= 1ull << (f % 64);
   }
   if (lf_status st = pooled_stride(g, n_kframes, &a.kf_stride, fn)) return st;
   if (!fits_int(static_cast<long long>(g.B) * g.H * a.kf_stride * g.d))

@@ -6,12 +6,20 @@
 
 namespace lf {
 
-constexpr int kMaxFrames = 256;   // key frames a frame-selecting call may address
+constexpr int kListFrames = 256;   // key frames whose id lists travel in the kernel arguments
+constexpr int kMaxFrames = 4096;   // key frames a frame-selecting call may address
 
-// Frame ids of the memory set M and of the always-kept frames, passed by value.
+// Frame ids of the memory set M and of the always-kept frames, passed by value (calls
+// with at most kListFrames key frames).
 struct FrameLists {
-  int16_t mem[kMaxFrames];
-  int16_t forced[kMaxFrames];
+  int16_t mem[kListFrames];
+  int16_t forced[kListFrames];
+};
+
+// The same two sets as bit masks (frame f is bit f % 64 of word f / 64), for any call.
+struct FrameMasks {
+  uint64_t mem[kMaxFrames / 64];
+  uint64_t forced[kMaxFrames / 64];
 };
 
 // x_stride: tokens between consecutive (b, h) slices of x; out_stride: frames between
@@ -83,7 +91,8 @@ struct SelectArgs {
   int n_qb, n_kframes, n_bpf;
   int kf_stride;        // frames between (b, h) slices of k_frm and k_blk
   int n_mem, n_forced, k_eff, W_f, kb_eff;
-  FrameLists lists;
+  FrameLists lists;     // filled when n_kframes <= kListFrames
+  FrameMasks masks;     // always filled by a frame-selecting call
 };
 
 hipError_t launch_select(const SelectArgs& a, int d, int n_rows, bool frames, bool blocks, hipStream_t st);

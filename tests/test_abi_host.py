@@ -134,7 +134,8 @@ def test_select_frames_validation():
     _err(call([1, 12], [0]), lf.LF_ERR_INVALID_ARG)            # out of range
     _err(call([], [], k_f=3), lf.LF_ERR_INVALID_ARG)           # empty T_r
     _err(call([1], [0], k_f=-1), lf.LF_ERR_INVALID_ARG)
-    _err(call([1], [0], n_kf=300), lf.LF_ERR_UNSUPPORTED)
+    _err(call([1], [0], n_kf=4097), lf.LF_ERR_UNSUPPORTED)              # beyond the 4096-frame limit
+    _err(call([1, 4000], [0], n_kf=3000), lf.LF_ERR_INVALID_ARG)        # long history: id out of range
     _err(call([1], [0], out=FAKE + 2), lf.LF_ERR_INVALID_ARG)
 
 
@@ -161,7 +162,8 @@ def test_select_fused_validation():
     _err(call([1], [0], k_b=0), lf.LF_ERR_INVALID_ARG)
     _err(call([1], [0], blocks=None), lf.LF_ERR_INVALID_ARG)
     _err(call([1], [0], frames=FAKE + 2), lf.LF_ERR_INVALID_ARG)
-    _err(call([1], [0], n_kf=300), lf.LF_ERR_UNSUPPORTED)
+    _err(call([1], [0], n_kf=4097), lf.LF_ERR_UNSUPPORTED)              # beyond the 4096-frame limit
+    _err(call([1, 4000], [0], n_kf=3000), lf.LF_ERR_INVALID_ARG)        # long history: id out of range
     _err(call([1], [0], gg=lf.Geom(1, 2, 128, 1560, 16)), lf.LF_ERR_UNSUPPORTED)   # 98 blocks per frame
 
 
