@@ -134,7 +134,11 @@ class PooledKeyCache:
     """Pooled keys of one layer for every frame of a clip: block means k~
     [B, H, n_frames*n_bpf, d] and frame means k^ [B, H, n_frames, d], fp32. Selection over
     the key prefix k_{:i} (Light Forcing summary, stage 3) reads the first frames; a
-    frame's entries are written when its keys are pooled."""
+    frame's block means are written when its keys are pooled, its frame mean by the next
+    chunk's pooling launch (or `complete_cache`). A steady-state chunk therefore expects
+    the block means of every earlier frame and the frame means of all but the previous
+    chunk's frames (filled by the earlier chunks, or by `lf_pool` for a history pooled at
+    once)."""
 
     def __init__(self, g: Geom, n_frames: int, device):
         self.geom, self.n_frames, self.nb = g, n_frames, n_bpf(g)
