@@ -586,7 +586,7 @@ def bench_sweep(args):
     # steady state: one pooled-key cache per layer; each chunk pools only its own key frames
     caches = [PooledKeyCache(g, sp.n_frames, dev) for _ in layers]
 
-    def run(events=None, cached=False):
+    def run(events=None, cached=False, stages=3):
         for li, (q, k, v) in enumerate(layers):
             mark = None
             if events is not None:
@@ -595,7 +595,24 @@ def bench_sweep(args):
                     ev.record(stream)
                     events.append((i, stage, ev))
             # the last chunk's frame means are read by no chunk of the sweep: not formed
-            sweep_layer(sw, q, k, v, o, mark, cache=caches[li] if cached else None, complete=False)
+            sweep_layer(sw, q, k, v, o, mark, cache=caches[li] if cached else None, complete=False, stages=stages)
+
+    def stages_in_loop(n, cached=False):
+        """Per-sweep stage times inside the sweep loop: n sweeps timed by HIP events around
+        the loop (queued behind a spin kernel) with the first 1, 2 and 3 stages of every
+        chunk, differenced (as for one chunk)."""
+        per = []
+        for upto in (1, 2, 3):
+            torch.cuda.synchronize()
+            hold_stream(60.0 * n)
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record(stream)
+            for _ in range(n):
+                run(cached=cached, stages=upto)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / n)
+        return {"pool": per[0], "select": per[1] - per[0], "attn": per[2] - per[1]}, per[2]
 
     def timed(cached):
         """(ms per sweep by wall clock, per-stage us, per-chunk us of one evented sweep)."""
@@ -628,9 +645,12 @@ def bench_sweep(args):
 
     ms_per_step, stage_us, chunk_us = timed(False)
     ss_ms, ss_stage, ss_chunk = timed(True)
+    n_loop = min(args.steps, 5)
+    loop_us, loop_sweep_us = stages_in_loop(n_loop)
+    ss_loop_us, _ = stages_in_loop(n_loop, cached=True)
     compare = compare_schedules(args, s, g, sp, sw, layers, o) if not args.no_extras else None
     ceiling = mfma_ceiling() if not args.no_extras else None
-    t_attn = stage_us["attn"] * 1e-6
+    t_attn = loop_us["attn"] * 1e-6
     attn_tflops = f_active / t_attn / 1e12
     cpu = None
     if args.cpu_heads > 0:
@@ -661,23 +681,29 @@ def bench_sweep(args):
                    "cag_s": [round(x, 6) for x in sp.s], "cag_beta": sp.beta,
                    "k_b": [c.k_b for c in sp.chunks], "W_b": [c.W_b for c in sp.chunks]},
         "mfma_pct_peak_active": 100.0 * attn_tflops / PEAK_BF16_TFLOPS,
-        "select_overhead_pct": 100.0 * stage_us["select"] / stage_us["attn"],
-        "pool_select_pct_of_attn": 100.0 * (sum(stage_us.values()) - stage_us["attn"]) / stage_us["attn"],
+        "select_overhead_pct": 100.0 * loop_us["select"] / loop_us["attn"],
+        "pool_select_pct_of_attn": 100.0 * (loop_us["pool"] + loop_us["select"]) / loop_us["attn"],
         "flops": {"dense_equiv": f_dense, "active": f_active, "block_density": f_active / f_dense},
-        "stage_us_per_sweep": {k: round(v, 1) for k, v in stage_us.items()},
-        "chunk_us_per_sweep": [round(x, 1) for x in chunk_us],
+        "stage_us_per_sweep_in_loop": {k: round(v, 1) for k, v in loop_us.items()},
+        "stage_us_per_sweep_in_loop_what": (f"{n_loop} sweeps with the first 1, 2, 3 stages of every chunk, HIP "
+                                            f"events around each loop on the launch stream, differenced"),
+        "stage_us_per_sweep_event_pairs": {k: round(v, 1) for k, v in stage_us.items()},
+        "chunk_us_per_sweep_event_pairs": [round(x, 1) for x in chunk_us],
         "steady_state": {
             "what": "per-layer pooled-key caches: each chunk pools its queries and only its own 3 key frames "
                     "(chunk 1 its keys only) and selects over the cached prefix",
             "value": f_dense / (ss_ms * 1e-3) / 1e12,
             "ms_per_step": ss_ms,
-            "stage_us_per_sweep": {k: round(v, 1) for k, v in ss_stage.items()},
-            "chunk_us_per_sweep": [round(x, 1) for x in ss_chunk],
-            "pool_select_pct_of_attn": 100.0 * (sum(ss_stage.values()) - ss_stage["attn"]) / ss_stage["attn"],
+            "stage_us_per_sweep_in_loop": {k: round(v, 1) for k, v in ss_loop_us.items()},
+            "stage_us_per_sweep_event_pairs": {k: round(v, 1) for k, v in ss_stage.items()},
+            "chunk_us_per_sweep_event_pairs": [round(x, 1) for x in ss_chunk],
+            "pool_select_pct_of_attn": 100.0 * (ss_loop_us["pool"] + ss_loop_us["select"]) / ss_loop_us["attn"],
         },
         "roofline": {"kernel": "attn_bf16_kernel<128>", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_of(s.name)},
+                     "traffic": traffic_of(s.name), "launch_us": round(loop_us["attn"] / (n_layers * s.n_chunks), 2),
+                     "timing": "mean per attention launch of the sweep (dense chunk 1 and sparse chunks 2-7), "
+                               "from the in-loop attention time per sweep"},
         "mfma_ceiling": ({**ceiling, "attn_frac_of_ceiling": attn_tflops / ceiling["tflops"]} if ceiling else None),
         "schedules": compare,
         "cpu_baseline": cpu,

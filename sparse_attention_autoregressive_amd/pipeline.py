@@ -300,7 +300,8 @@ class SweepWorkspace:
 
 
 def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                o: torch.Tensor, mark=None, cache: PooledKeyCache = None, complete: bool = True) -> torch.Tensor:
+                o: torch.Tensor, mark=None, cache: PooledKeyCache = None, complete: bool = True,
+                stages: int = 3) -> torch.Tensor:
     """All chunks of one layer in order. q, k, v, o: [B, H, n_frames*tpf, d] holding the
     whole clip; chunk i reads its query frames and the key prefix as views and writes its
     frames of o. Enqueued on the current stream; returns o. `mark(i, stage)`, if given,
@@ -309,7 +310,9 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
     sized for the clip), every chunk pools only its own key frames into it, the dense
     first chunk included, and selection reads the cached prefix: the same outputs. The
     cache then holds every frame's means on return (the last chunk's frame means are
-    formed after its attention, by `complete_cache`), unless `complete` is False."""
+    formed after its attention, by `complete_cache`), unless `complete` is False.
+    `stages` < 3 runs only the first stages of every chunk (1: pooling, 2: pooling and
+    selection), for timing the stages apart; o is then not written."""
     sp = sw.plan
     tpf = sp.geom.tokens_per_frame
     tick = mark if mark is not None else (lambda i, stage: None)
@@ -320,21 +323,24 @@ def sweep_layer(sw: SweepWorkspace, q: torch.Tensor, k: torch.Tensor, v: torch.T
             if cache is not None:
                 tick(i, "pool")
                 pool_keys_cached(p, cache, kv)
-            tick(i, "attn")
-            lf_sparse_attn(qv, kv, vv, p.geom, p.n_qframes, p.n_kframes, sw.full[i], p.scale, out=ov)
+            if stages >= 3:
+                tick(i, "attn")
+                lf_sparse_attn(qv, kv, vv, p.geom, p.n_qframes, p.n_kframes, sw.full[i], p.scale, out=ov)
         else:
             tick(i, "pool")
             if cache is None:
                 pool(ws, qv, kv)
             else:
                 pool_cached(ws, cache, qv, kv)
-            tick(i, "select")
-            if cache is None:
-                select(ws)
-            else:
-                select_cached(ws, cache)
-            tick(i, "attn")
-            attend(ws, qv, kv, vv, ov)
+            if stages >= 2:
+                tick(i, "select")
+                if cache is None:
+                    select(ws)
+                else:
+                    select_cached(ws, cache)
+            if stages >= 3:
+                tick(i, "attn")
+                attend(ws, qv, kv, vv, ov)
         tick(i, "end")
     if cache is not None and complete and sp.chunks:
         complete_cache(sp.chunks[-1], cache)
