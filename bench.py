@@ -459,6 +459,11 @@ def main():
     # active FLOPs per attention launch of the loop (the input sets' lists differ slightly)
     f_sets = [flops_of(w, ws.blocks.cpu().numpy())[1] for ws in wss]
     f_active_loop = float(np.mean([f_sets[i % len(sets)] for i in range(args.steps)]))
+    # algorithmic HBM bytes of one attention launch: Q read, O written, each K/V token of the
+    # prefix read once (an upper bound of the unique bytes: a key block no row lists is not
+    # read)
+    esz = 2 if w.dtype == "bf16" else 4
+    attn_bytes = w.B * w.H * (2 * w.lq + 2 * w.lk) * w.d * esz
     t_attn = attn_loop_us * 1e-6
     t_path = loop_step_us * 1e-6
     attn_tflops = f_active_loop / t_attn / 1e12
@@ -540,6 +545,9 @@ def main():
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_of(w.name),
+                     "algorithmic_bytes_upper": attn_bytes,
+                     "traffic_over_algorithmic": (round(traffic_of(w.name) / attn_bytes, 3)
+                                                  if traffic_of(w.name) else None),
                      "launch_us": round(attn_loop_us, 2), "active_flops_per_launch": f_active_loop,
                      "timing": (f"{args.steps} steps timed by HIP events around the loop on the launch "
                                 f"stream, with and without the attention launch (difference)")},
