@@ -382,8 +382,9 @@ def test_edge_lists_longer_than_one_segment():
 
 
 def test_edge_maximum_frame_count():
-    # 256 key frames (the selection limit) of one 16-token block each; 252 memory frames
-    # ranked per row
+    # 256 key frames (the most the listed frame stage takes; beyond, the long-history path,
+    # tests/test_gpu_long_history.py) of one 16-token block each; 252 memory frames ranked
+    # per row
     w = _base(tpf=16, bs=16, n_kframes=256, current=(253, 254, 255), sink=(0,), recent=(252,),
               mem=tuple(range(1, 252)), k_f=8, k_b=1, q_pool=tuple(range(0, 252)), name="max_frames", seed=7011)
     _edge(w)
