@@ -451,6 +451,7 @@ def main():
 
     extras = not args.no_extras
     one_level = compare_one_level(args, w, g, plan, wss[0], sets[0]) if extras else None
+    scaling = select_scaling(args, w, g) if extras and w.d in (64, 128) else None
     prologue = compare_prologue(args, w, g, plan, sets[0]) if extras else None
     ceiling = mfma_ceiling() if extras else None
     hbm = hbm_ceiling() if extras else None
@@ -540,6 +541,7 @@ def main():
                         if hbm else None),
         "steady_state": steady,
         "one_level": one_level,
+        "select_scaling": scaling,
         "prologue": prologue,
         "roofline": {"kernel": "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>",
                      "bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
@@ -775,6 +777,36 @@ def compare_prologue(args, w, g, plan, qkv):
             "algorithmic_bytes": moved,
             "two_calls_us": round(t_two, 2), "two_calls_hbm_gbs": round(moved_two / (t_two * 1e-6) / 1e9, 1),
             "separate_pool_pass_us": round(t_pool, 2)}
+
+
+def select_scaling(args, w, g):
+    """The fused selection call over growing histories at this layer's geometry (the
+    chunk's query blocks; k_f and k_b as configured; 3 current frames and a sink frame
+    always kept, every other frame in M): per-call time for several key-frame counts.
+    Attention over the resulting lists has a fixed width (W_b), so it stays constant while
+    the frame stage grows with |M|. Pooled tensors are random fp32 drawn on the device
+    (timing only)."""
+    dev = torch.device("cuda")
+    nb = lf.n_bpf(g)
+    n_qb = w.n_qframes * nb
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    q_blk = torch.randn((w.B, w.H, n_qb, w.d), generator=gen, device=dev)
+    res = {}
+    for n in (21, 69, 300, 1200, 4096):
+        k_frm = torch.randn((w.B, w.H, n, w.d), generator=gen, device=dev)
+        k_blk = torch.randn((w.B, w.H, n * nb, w.d), generator=gen, device=dev)
+        forced = [0, n - 3, n - 2, n - 1]
+        mem = list(range(1, n - 3))
+        k_f, k_b = w.k_f, min(w.k_b or 8, nb)
+        fo, bo = lf.lf_select(q_blk, k_frm, k_blk, g, n_qb, n, mem, forced, k_f, k_b)
+        reps = max(5, min(args.steps, 30))
+        t = per_call(lambda: lf.lf_select(q_blk, k_frm, k_blk, g, n_qb, n, mem, forced, k_f, k_b, fo, bo), reps)
+        res[str(n)] = round(t, 2)
+        del k_frm, k_blk
+    torch.cuda.empty_cache()
+    return {"what": (f"lf_select at {w.name}'s geometry ({w.B * w.H * n_qb} rows), |M| = n - 4, k_f = {w.k_f}: "
+                     f"us per call by key frames n"), "us_by_key_frames": res}
 
 
 def compare_one_level(args, w, g, plan, ws, qkv):
