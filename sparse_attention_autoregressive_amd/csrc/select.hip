@@ -57,18 +57,26 @@ struct QSlice {
   float4 v[D / 32];
 };
 
+// Inner product of the group's q~ slices with the matching slices k of a key row.
 template <int D>
-__device__ __forceinline__ float group_dot(const QSlice<D>& q, const float* __restrict__ row, int c) {
+__device__ __forceinline__ float slice_dot(const QSlice<D>& q, const float4 (&k)[D / 32]) {
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
-    const float4 k = *reinterpret_cast<const float4*>(row + 4 * c + 32 * i);
-    a0 = fmaf(q.v[i].x, k.x, a0);
-    a1 = fmaf(q.v[i].y, k.y, a1);
-    a0 = fmaf(q.v[i].z, k.z, a0);
-    a1 = fmaf(q.v[i].w, k.w, a1);
+    a0 = fmaf(q.v[i].x, k[i].x, a0);
+    a1 = fmaf(q.v[i].y, k[i].y, a1);
+    a0 = fmaf(q.v[i].z, k[i].z, a0);
+    a1 = fmaf(q.v[i].w, k[i].w, a1);
   }
   return group_sum(a0 + a1);
+}
+
+template <int D>
+__device__ __forceinline__ float group_dot(const QSlice<D>& q, const float* __restrict__ row, int c) {
+  float4 k[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) k[i] = *reinterpret_cast<const float4*>(row + 4 * c + 32 * i);
+  return slice_dot<D>(q, k);
 }
 
 // Number of keys among keys[0..n) above `mine` (keys are distinct).
@@ -93,48 +101,65 @@ __device__ __forceinline__ int frame_at(const TS* t_s, const SelectArgs& a, int 
   return FRAMES ? t_s[t] : min(max(a.frames_in[static_cast<size_t>(row) * W_f + t], 0), a.n_kframes - 1);
 }
 
-// Block stage of one row: T_r's frames (t_s, or the caller's list), up to kSlots per
-// pass, each frame's n_bpf block scores ranked and the chosen ids written ascending.
-template <int D, bool FRAMES, typename TS>
-__device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D>& q, int row, int bh, int W_f,
-                                            const TS* t_s, uint64_t (*bkey_s)[64]) {
+// Block stage of nr <= R rows of one head: each row's T_r (t_s + rr * W_f, or the
+// caller's list), kSlots / R frames of every row per pass, each frame's n_bpf block
+// scores ranked and the chosen ids written ascending. Group g scores the blocks of row
+// g % R with that row's q~ slices, so the R rows share each pass and its barriers.
+template <int D, int R, bool FRAMES, typename TS>
+__device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D> (&q)[R], int row0, int nr, int bh,
+                                            int W_f, const TS* t_s, uint64_t (*bkey_s)[64]) {
+  constexpr int S = kSlots / R;                    // frames of each row per pass
+  constexpr int GR = kGroups / R;                  // groups per row
+  static_assert(kSlots % R == 0 && kGroups % R == 0, "rows divide the pass");
+  if (R == 1) nr = 1;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int grp = threadIdx.x / kGroup, c = threadIdx.x % kGroup;
   const uint64_t below = lanes_below_mask();
   const int n_bpf = a.n_bpf, kb = a.kb_eff;
-  int* out = a.blocks_out + static_cast<size_t>(row) * W_f * kb;
+  auto frame = [&](int rr, int t) { return frame_at<FRAMES>(t_s + rr * W_f, a, row0 + rr, W_f, t); };
+  auto out = [&](int rr) { return a.blocks_out + static_cast<size_t>(row0 + rr) * W_f * kb; };
   if (kb >= n_bpf) {                               // every block of every frame is kept
-    for (int i = threadIdx.x; i < W_f * n_bpf; i += kSelThreads) {
-      const int t = i / n_bpf, j = i - t * n_bpf;
-      out[t * kb + j] = frame_at<FRAMES>(t_s, a, row, W_f, t) * n_bpf + j;
+    for (int i = threadIdx.x; i < nr * W_f * n_bpf; i += kSelThreads) {
+      const int u = i / n_bpf, j = i - u * n_bpf;
+      const int rr = R == 1 ? 0 : u / W_f, t = u - rr * W_f;
+      out(rr)[t * kb + j] = frame(rr, t) * n_bpf + j;
     }
     return;
   }
+  const int gr = grp % R, gi = grp / R;
+  QSlice<D> qg = q[0];
+#pragma unroll
+  for (int rr = 1; rr < R; ++rr)
+    if (gr == rr) qg = q[rr];
   const float* kbase = a.k_blk + static_cast<size_t>(bh) * a.kf_stride * n_bpf * D;
-  for (int t0 = 0; t0 < W_f; t0 += kSlots) {
-    const int nt = min(kSlots, W_f - t0);
-    for (int e = grp; e < nt * n_bpf; e += kGroups) {
-      const int t = e / n_bpf, j = e - t * n_bpf;
-      const float s = group_dot<D>(q, kbase + (static_cast<size_t>(frame_at<FRAMES>(t_s, a, row, W_f, t0 + t)) * n_bpf + j) * D, c);
-      if (c == 0) bkey_s[t][j] = rank_key(s, static_cast<uint32_t>(j));
+  for (int t0 = 0; t0 < W_f; t0 += S) {
+    const int nt = min(S, W_f - t0);
+    if (gr < nr) {
+      for (int e = gi; e < nt * n_bpf; e += GR) {
+        const int t = e / n_bpf, j = e - t * n_bpf;
+        const float s = group_dot<D>(qg, kbase + (static_cast<size_t>(frame(gr, t0 + t)) * n_bpf + j) * D, c);
+        if (c == 0) bkey_s[gr * S + t][j] = rank_key(s, static_cast<uint32_t>(j));
+      }
     }
     __syncthreads();
+    const int ns = nr * nt;                        // slot u: row u / nt, frame t0 + u % nt
     if (n_bpf <= 32) {
-      // two frames per wave at once: lanes 0-31 rank slot tb, lanes 32-63 slot tb + 1
+      // two frames per wave at once: lanes 0-31 rank slot ub, lanes 32-63 slot ub + 1
       const int half = lane >> 5, jl = lane & 31;
       const uint64_t below_half = jl == 0 ? 0ull : (~0ull >> (64 - jl)) << (32 * half);
-      for (int tb = 2 * wave; tb < nt; tb += 2 * kSelWaves) {
-        const int t = tb + half;
-        const bool on = t < nt && jl < n_bpf && rank_of(bkey_s[t][jl], bkey_s[t], n_bpf) < kb;
+      for (int ub = 2 * wave; ub < ns; ub += 2 * kSelWaves) {
+        const int u = ub + half;
+        const int rr = R == 1 ? 0 : u / nt, t = u - rr * nt;
+        const bool on = u < ns && jl < n_bpf && rank_of(bkey_s[rr * S + t][jl], bkey_s[rr * S + t], n_bpf) < kb;
         const uint64_t m = __ballot(on);
-        if (on) out[(t0 + t) * kb + __popcll(m & below_half)] = frame_at<FRAMES>(t_s, a, row, W_f, t0 + t) * n_bpf + jl;
+        if (on) out(rr)[(t0 + t) * kb + __popcll(m & below_half)] = frame(rr, t0 + t) * n_bpf + jl;
       }
     } else {
-      for (int t = wave; t < nt; t += kSelWaves) {
-        const bool mine = lane < n_bpf;
-        const bool on = mine && rank_of(bkey_s[t][lane], bkey_s[t], n_bpf) < kb;
+      for (int u = wave; u < ns; u += kSelWaves) {
+        const int rr = R == 1 ? 0 : u / nt, t = u - rr * nt;
+        const bool on = lane < n_bpf && rank_of(bkey_s[rr * S + t][lane], bkey_s[rr * S + t], n_bpf) < kb;
         const uint64_t m = __ballot(on);
-        if (on) out[(t0 + t) * kb + __popcll(m & below)] = frame_at<FRAMES>(t_s, a, row, W_f, t0 + t) * n_bpf + lane;
+        if (on) out(rr)[(t0 + t) * kb + __popcll(m & below)] = frame(rr, t0 + t) * n_bpf + lane;
       }
     }
     __syncthreads();
@@ -206,121 +231,228 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
     __syncthreads();
   }
 
-  block_stage<D, FRAMES>(a, q, row, bh, W_f, t_s, bkey_s);
+  const QSlice<D> q1[1] = {q};
+  block_stage<D, 1, FRAMES>(a, q1, row, 1, bh, W_f, t_s, bkey_s);
 }
 
-// Frame stage for calls with more than kListFrames key frames (long histories): M and the
-// always-kept frames arrive as bit masks and wave 0 expands them in LDS (ascending ids);
-// the ids, keys, flags and T_r live in dynamic LDS sized for the call. Frame scores are
-// the same 8-lane inner products as above; the top k_eff keys are taken in k_eff rounds,
-// each the block-wide maximum of the keys below the previous round's (keys are distinct,
-// and a key carries its frame id), so a round costs one pass over |M| / 256 keys per
-// thread rather than a rank count over all |M| keys. Results equal the listed kernel's.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+// Maximum (MAX) or minimum of x over the wave, in every lane: within rows of 16 lanes by
+// DPP moves (pairs, quads, half rows, rows), then across row pairs and wave halves.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+template <bool MAX>
+__device__ __forceinline__ uint32_t pick(uint32_t x, uint32_t y) {
+  return MAX ? max(x, y) : min(x, y);
+}
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
+  x = pick<MAX>(x, dpp_u32<0xB1>(x));    // quad_perm [1, 0, 3, 2]
+  x = pick<MAX>(x, dpp_u32<0x4E>(x));    // quad_perm [2, 3, 0, 1]
+  x = pick<MAX>(x, dpp_u32<0x141>(x));   // row_half_mirror
+  x = pick<MAX>(x, dpp_u32<0x140>(x));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = pick<MAX>(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return pick<MAX>(b[0], b[1]);
+}
+
+// Sum of x over the lanes below this one.
+__device__ __forceinline__ int wave_excl_sum(int x) {
+  const int lane = threadIdx.x % kWave;
+  int s = x;
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) {
-    const uint64_t y = __shfl_xor(x, m, kWave);
-    x = y > x ? y : x;
+    const int y = __shfl_up(s, m, kWave);
+    if (lane >= m) s += y;
   }
-  return x;
+  return s - x;
 }
 
-template <int D, bool BLOCKS>
+// LDS layout of select_long_kernel, in bytes from the start of dynamic LDS.
+struct LongLds {
+  int n_words, sc_stride;                // mask words per row; score entries per row (even)
+  size_t bits, t, mem, total;            // offsets of the row bits, T_r, the ids of M; size
+};
+__host__ __device__ inline LongLds long_lds(int R, int n_mem, int n_kframes, int W_f, bool keep_all) {
+  LongLds L;
+  L.n_words = (n_kframes + 63) / 64;
+  L.sc_stride = (n_mem + 1) & ~1;
+  L.bits = keep_all ? 0 : static_cast<size_t>(R) * L.sc_stride * 4;
+  L.t = L.bits + static_cast<size_t>(R) * L.n_words * 8;
+  L.mem = L.t + static_cast<size_t>(R) * W_f * 2;
+  L.total = L.mem + static_cast<size_t>(n_mem) * 2;
+  return L;
+}
+
+// Selection for calls with more than kListFrames key frames (long histories).
+// - M and the always-kept frames arrive as bit masks; wave 0 takes one 64-frame word per
+//   lane and expands M into LDS in ascending order (a prefix count of the words'
+//   populations gives each lane its first position).
+// - A workgroup takes kLongRows consecutive rows of one head. Every row scores the same
+//   frames of M, so each frame mean an 8-lane group loads is dotted with both rows' q~
+//   slices (the same group inner product, term for term, as the listed kernel's), which
+//   halves the frame means' L2 traffic; each group keeps kLongUnroll frame means in
+//   flight. Scores are stored as 32-bit order-preserving bits per row.
+// - Wave w takes row w's top k_eff: the row's scores sit in registers (lane l holds
+//   positions l + 64 i of M), and each round takes the largest remaining score -- at its
+//   lowest position when several are equal, which ranks M as the listed kernel's
+//   (score, lower frame id first) keys do, since positions ascend with frame ids -- sets
+//   the frame's bit over the always-kept frames' bits and clears the score.
+// - Each row's bits are compacted into T_r by the same prefix count, and both rows' block
+//   stages share passes (block_stage with two rows).
+constexpr int kLongUnroll = 4;                     // frame means in flight per group
+constexpr int kLongRows = 2;                       // rows per workgroup
+
+template <int D, int NP, bool BLOCKS>
 __global__ void __launch_bounds__(kSelThreads) select_long_kernel(SelectArgs a) {
+  constexpr int R = kLongRows;
+  static_assert(R >= 1 && R <= kSelWaves, "one row per wave in the top-k rounds");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_s[];
   __shared__ uint64_t bkey_s[kSlots][64];
-  __shared__ uint64_t max_s[2][kSelWaves];
-  const int n_mem = a.n_mem, n_kf = a.n_kframes, W_f = a.W_f;
-  // dynamic LDS: keys [n_mem] | T_r [W_f] | ids of M [n_mem] | flags [n_kframes]
-  uint64_t* keys_s = reinterpret_cast<uint64_t*>(dyn_s);
-  int16_t* t_s = reinterpret_cast<int16_t*>(keys_s + n_mem);
-  int16_t* mem_s = t_s + W_f;
-  unsigned char* flag_s = reinterpret_cast<unsigned char*>(mem_s + n_mem);
+  const int n_mem = a.n_mem, W_f = a.W_f;
+  const bool keep_all = a.k_eff >= n_mem;
+  const LongLds L = long_lds(R, n_mem, a.n_kframes, W_f, keep_all);
+  uint32_t* sc_s = reinterpret_cast<uint32_t*>(dyn_s);
+  uint64_t* bits_s = reinterpret_cast<uint64_t*>(dyn_s + L.bits);
+  int16_t* t_s = reinterpret_cast<int16_t*>(dyn_s + L.t);
+  int16_t* mem_s = reinterpret_cast<int16_t*>(dyn_s + L.mem);
 
+  // R rows of one head per workgroup, head-major over the XCDs
+  const int groups = (a.n_qb + R - 1) / R;
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int per = nwg / 8, rem = nwg % 8;
-  const int row = xcd * per + min(xcd, rem) + slot;
-  const int bh = row / a.n_qb;
+  const int gid = xcd * per + min(xcd, rem) + slot;
+  const int bh = gid / groups, j0 = (gid - bh * groups) * R;
+  const int row0 = bh * a.n_qb + j0, nr = min(R, a.n_qb - j0);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int grp = threadIdx.x / kGroup, c = threadIdx.x % kGroup;
-  const uint64_t below = lanes_below_mask();
 
-  QSlice<D> q;
-  {
-    const float* qr = a.q_blk + static_cast<size_t>(row) * D;
+  QSlice<D> q[R];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) q.v[i] = *reinterpret_cast<const float4*>(qr + 4 * c + 32 * i);
+  for (int rr = 0; rr < R; ++rr) {
+    const float* qr = a.q_blk + static_cast<size_t>(row0 + min(rr, nr - 1)) * D;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) q[rr].v[i] = *reinterpret_cast<const float4*>(qr + 4 * c + 32 * i);
   }
+  for (int i = threadIdx.x; i < R * W_f; i += kSelThreads) t_s[i] = 0;   // every T_r entry a valid id
   if (wave == 0) {
-    int mcount = 0;
-    for (int f0 = 0; f0 < n_kf; f0 += kWave) {
-      const uint64_t mw = a.masks.mem[f0 / kWave], fw = a.masks.forced[f0 / kWave];
-      const int f = f0 + lane;
-      if (f < n_kf) flag_s[f] = static_cast<unsigned char>((fw >> lane) & 1ull);
-      if ((mw >> lane) & 1ull) mem_s[mcount + __popcll(mw & below)] = static_cast<int16_t>(f);
-      mcount += __popcll(mw);
+    const uint64_t mw = lane < L.n_words ? a.masks.mem[lane] : 0ull;
+    const uint64_t fw = lane < L.n_words ? a.masks.forced[lane] : 0ull;
+    int pos = wave_excl_sum(__popcll(mw));
+    for (uint64_t m = mw; m; m &= m - 1) mem_s[pos++] = static_cast<int16_t>(64 * lane + __builtin_ctzll(m));
+    if (lane < L.n_words) {
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) bits_s[rr * L.n_words + lane] = keep_all ? (fw | mw) : fw;
     }
   }
   __syncthreads();
-  const bool keep_all = a.k_eff >= n_mem;
-  if (keep_all) {
-    for (int e = threadIdx.x; e < n_mem; e += kSelThreads) flag_s[mem_s[e]] = 1;
-  } else {
+  if (!keep_all) {
+    // kLongUnroll frame means per group in flight: each group walks ~|M| / 32 frames
     const float* kf = a.k_frm + static_cast<size_t>(bh) * a.kf_stride * D;
-    for (int e = grp; e < n_mem; e += kGroups) {
-      const int f = mem_s[e];
-      const float s = group_dot<D>(q, kf + static_cast<size_t>(f) * D, c);
-      if (c == 0) keys_s[e] = rank_key(s, static_cast<uint32_t>(f));
+    for (int e0 = grp; e0 < n_mem; e0 += kLongUnroll * kGroups) {
+      float4 k[kLongUnroll][D / 32];
+#pragma unroll
+      for (int u = 0; u < kLongUnroll; ++u) {
+        const float* kr = kf + static_cast<size_t>(mem_s[min(e0 + u * kGroups, n_mem - 1)]) * D;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) k[u][i] = *reinterpret_cast<const float4*>(kr + 4 * c + 32 * i);
+      }
+#pragma unroll
+      for (int u = 0; u < kLongUnroll; ++u) {
+        const int e = e0 + u * kGroups;
+        if (e >= n_mem) break;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          if (rr < nr) {
+            const float s = slice_dot<D>(q[rr], k[u]);
+            if (c == 0) sc_s[rr * L.sc_stride + e] = max(ordered_bits(s), 1u);   // 0 marks a taken entry
+          }
+        }
+      }
     }
     __syncthreads();
-    uint64_t bound = ~0ull;
-    for (int r = 0; r < a.k_eff; ++r) {
-      uint64_t best = 0;
-      for (int e = threadIdx.x; e < n_mem; e += kSelThreads) {
-        const uint64_t k = keys_s[e];
-        if (k < bound && k > best) best = k;
-      }
-      best = wave_max_u64(best);
-      if (lane == 0) max_s[r & 1][wave] = best;
-      __syncthreads();
-      bound = max_s[r & 1][0];
+    if (wave < nr) {
+      // the row's scores in registers, element i of a lane at position lane + 64 i of M
+      // (NP * 64 >= |M|; empty places hold 0, below every score). A round takes the
+      // largest remaining score, at its lowest position when several lanes hold it, and
+      // clears it.
+      const uint32_t* scr = sc_s + wave * L.sc_stride;
+      uint32_t sc[NP];
 #pragma unroll
-      for (int w = 1; w < kSelWaves; ++w) bound = max_s[r & 1][w] > bound ? max_s[r & 1][w] : bound;
-      if (threadIdx.x == 0) flag_s[key_id(bound)] = 1;
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int count = 0;
-    for (int f0 = 0; f0 < n_kf; f0 += kWave) {
-      const int f = f0 + lane;
-      const bool on = f < n_kf && flag_s[f] != 0;
-      const uint64_t m = __ballot(on);
-      const int pos = count + __popcll(m & below);
-      if (on) {
-        t_s[pos] = static_cast<int16_t>(f);
-        if (a.frames_out) a.frames_out[static_cast<size_t>(row) * W_f + pos] = f;
+      for (int i = 0; i < NP; ++i) {
+        const int e = lane + kWave * i;
+        sc[i] = e < n_mem ? scr[e] : 0u;
       }
-      count += __popcll(m);
+      for (int r = 0; r < a.k_eff; ++r) {
+        uint32_t best = 0;
+        int bi = 0;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const bool gt = sc[i] > best;
+          best = gt ? sc[i] : best;
+          bi = gt ? i : bi;
+        }
+        const uint32_t top = wave_reduce<true>(best);
+        const int win = min(static_cast<int>(wave_reduce<false>(best == top ? static_cast<uint32_t>(lane + kWave * bi)
+                                                                            : 0xFFFFFFFFu)),
+                            n_mem - 1);
+        const int dw = win - lane;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) sc[i] = dw == kWave * i ? 0u : sc[i];
+        if (lane == 0) {
+          const int f = mem_s[win];
+          bits_s[wave * L.n_words + f / 64] |= 1ull << (f % 64);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (wave < nr) {
+    const uint64_t w = lane < L.n_words ? bits_s[wave * L.n_words + lane] : 0ull;
+    int pos = wave_excl_sum(__popcll(w));
+    int16_t* t = t_s + wave * W_f;
+    int* fo = a.frames_out ? a.frames_out + static_cast<size_t>(row0 + wave) * W_f : nullptr;
+    for (uint64_t m = w; m && pos < W_f; m &= m - 1, ++pos) {
+      const int f = 64 * lane + __builtin_ctzll(m);
+      t[pos] = static_cast<int16_t>(f);
+      if (fo) fo[pos] = f;
     }
   }
   if (!BLOCKS) return;
   __syncthreads();
-  block_stage<D, true>(a, q, row, bh, W_f, t_s, bkey_s);
+  block_stage<D, R, true>(a, q, row0, nr, bh, W_f, t_s, bkey_s);
 }
 
-// Dynamic LDS of select_long_kernel.
-static size_t long_select_lds(const SelectArgs& a) {
-  return static_cast<size_t>(a.n_mem) * 8 + static_cast<size_t>(a.W_f) * 2 + static_cast<size_t>(a.n_mem) * 2 +
-         static_cast<size_t>(a.n_kframes);
+constexpr size_t kLongLdsMax = 160 * 1024 - sizeof(uint64_t) * kSlots * 64;
+
+template <int D, int NP, bool BLOCKS>
+static hipError_t launch_select_long_np(const SelectArgs& a, int n_rows, hipStream_t st) {
+  const int n_bh = n_rows / a.n_qb, groups = (a.n_qb + kLongRows - 1) / kLongRows;
+  const size_t lds = long_lds(kLongRows, a.n_mem, a.n_kframes, a.W_f, a.k_eff >= a.n_mem).total;
+  if (lds > kLongLdsMax) return hipErrorInvalidValue;
+  if (lds > 64 * 1024) {
+    // dynamic LDS past 64 KB is declared for the kernel (up to the 160 KB a workgroup can
+    // address); a runtime that does not need the declaration may refuse it, so its status
+    // is cleared and the launch's own status decides
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&select_long_kernel<D, NP, BLOCKS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLongLdsMax));
+    (void)hipGetLastError();
+  }
+  hipLaunchKernelGGL((select_long_kernel<D, NP, BLOCKS>), dim3(static_cast<unsigned>(n_bh * groups)),
+                     dim3(kSelThreads), static_cast<unsigned>(lds), st, a);
+  return hipGetLastError();
 }
 
+// Scores per lane in the top-k rounds: the smallest of 8, 16, 32, 64 that covers M.
 template <int D, bool BLOCKS>
 static hipError_t launch_select_long_d(const SelectArgs& a, int n_rows, hipStream_t st) {
-  hipLaunchKernelGGL((select_long_kernel<D, BLOCKS>), dim3(static_cast<unsigned>(n_rows)), dim3(kSelThreads),
-                     static_cast<unsigned>(long_select_lds(a)), st, a);
-  return hipGetLastError();
+  static_assert(kMaxFrames <= 64 * kWave, "64 scores per lane cover every memory set");
+  if (a.n_mem <= 8 * kWave) return launch_select_long_np<D, 8, BLOCKS>(a, n_rows, st);
+  if (a.n_mem <= 16 * kWave) return launch_select_long_np<D, 16, BLOCKS>(a, n_rows, st);
+  if (a.n_mem <= 32 * kWave) return launch_select_long_np<D, 32, BLOCKS>(a, n_rows, st);
+  return launch_select_long_np<D, 64, BLOCKS>(a, n_rows, st);
 }
 
 template <int D, bool FRAMES, bool BLOCKS>
