@@ -105,7 +105,7 @@ __device__ __forceinline__ int frame_at(const TS* t_s, const SelectArgs& a, int 
 // caller's list), kSlots / R frames of every row per pass, each frame's n_bpf block
 // scores ranked and the chosen ids written ascending. Group g scores the blocks of row
 // g % R with that row's q~ slices, so the R rows share each pass and its barriers.
-template <int D, int R, bool FRAMES, typename TS>
+template <int D, int R, bool FRAMES, int U = 1, typename TS>
 __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D> (&q)[R], int row0, int nr, int bh,
                                             int W_f, const TS* t_s, uint64_t (*bkey_s)[64]) {
   constexpr int S = kSlots / R;                    // frames of each row per pass
@@ -135,10 +135,25 @@ __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D>
   for (int t0 = 0; t0 < W_f; t0 += S) {
     const int nt = min(S, W_f - t0);
     if (gr < nr) {
-      for (int e = gi; e < nt * n_bpf; e += GR) {
-        const int t = e / n_bpf, j = e - t * n_bpf;
-        const float s = group_dot<D>(qg, kbase + (static_cast<size_t>(frame(gr, t0 + t)) * n_bpf + j) * D, c);
-        if (c == 0) bkey_s[gr * S + t][j] = rank_key(s, static_cast<uint32_t>(j));
+      // U block means per group in flight
+      const int ne = nt * n_bpf;
+      for (int e0 = gi; e0 < ne; e0 += U * GR) {
+        float4 k[U][D / 32];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = min(e0 + u * GR, ne - 1), t = e / n_bpf, j = e - t * n_bpf;
+          const float* kr = kbase + (static_cast<size_t>(frame(gr, t0 + t)) * n_bpf + j) * D;
+#pragma unroll
+          for (int i = 0; i < D / 32; ++i) k[u][i] = *reinterpret_cast<const float4*>(kr + 4 * c + 32 * i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + u * GR;
+          if (e >= ne) break;
+          const int t = e / n_bpf, j = e - t * n_bpf;
+          const float s = slice_dot<D>(qg, k[u]);
+          if (c == 0) bkey_s[gr * S + t][j] = rank_key(s, static_cast<uint32_t>(j));
+        }
       }
     }
     __syncthreads();
@@ -303,6 +318,7 @@ __host__ __device__ inline LongLds long_lds(int R, int n_mem, int n_kframes, int
 //   stages share passes (block_stage with two rows).
 constexpr int kLongUnroll = 4;                     // frame means in flight per group
 constexpr int kLongRows = 2;                       // rows per workgroup
+constexpr int kLongBlockUnroll = 2;                // block means in flight per group
 
 template <int D, int NP, bool BLOCKS>
 __global__ void __launch_bounds__(kSelThreads) select_long_kernel(SelectArgs a) {
@@ -422,7 +438,7 @@ __global__ void __launch_bounds__(kSelThreads) select_long_kernel(SelectArgs a) 
   }
   if (!BLOCKS) return;
   __syncthreads();
-  block_stage<D, R, true>(a, q, row0, nr, bh, W_f, t_s, bkey_s);
+  block_stage<D, R, true, kLongBlockUnroll>(a, q, row0, nr, bh, W_f, t_s, bkey_s);
 }
 
 constexpr size_t kLongLdsMax = 160 * 1024 - sizeof(uint64_t) * kSlots * 64;
