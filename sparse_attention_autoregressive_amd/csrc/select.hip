@@ -105,12 +105,13 @@ __device__ __forceinline__ int frame_at(const TS* t_s, const SelectArgs& a, int 
 // caller's list), kSlots / R frames of every row per pass, each frame's n_bpf block
 // scores ranked and the chosen ids written ascending. Group g scores the blocks of row
 // g % R with that row's q~ slices, so the R rows share each pass and its barriers.
-template <int D, int R, bool FRAMES, int U = 1, typename TS>
+template <int D, int R, bool FRAMES, int U = 1, int T = kSelThreads, int SLOTS = kSlots, typename TS>
 __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D> (&q)[R], int row0, int nr, int bh,
                                             int W_f, const TS* t_s, uint64_t (*bkey_s)[64]) {
-  constexpr int S = kSlots / R;                    // frames of each row per pass
-  constexpr int GR = kGroups / R;                  // groups per row
-  static_assert(kSlots % R == 0 && kGroups % R == 0, "rows divide the pass");
+  constexpr int WAVES = T / kWave, GROUPS = T / kGroup;
+  constexpr int S = SLOTS / R;                     // frames of each row per pass
+  constexpr int GR = GROUPS / R;                   // groups per row
+  static_assert(SLOTS % R == 0 && GROUPS % R == 0, "rows divide the pass");
   if (R == 1) nr = 1;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int grp = threadIdx.x / kGroup, c = threadIdx.x % kGroup;
@@ -119,7 +120,7 @@ __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D>
   auto frame = [&](int rr, int t) { return frame_at<FRAMES>(t_s + rr * W_f, a, row0 + rr, W_f, t); };
   auto out = [&](int rr) { return a.blocks_out + static_cast<size_t>(row0 + rr) * W_f * kb; };
   if (kb >= n_bpf) {                               // every block of every frame is kept
-    for (int i = threadIdx.x; i < nr * W_f * n_bpf; i += kSelThreads) {
+    for (int i = threadIdx.x; i < nr * W_f * n_bpf; i += T) {
       const int u = i / n_bpf, j = i - u * n_bpf;
       const int rr = R == 1 ? 0 : u / W_f, t = u - rr * W_f;
       out(rr)[t * kb + j] = frame(rr, t) * n_bpf + j;
@@ -162,7 +163,7 @@ __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D>
       // two frames per wave at once: lanes 0-31 rank slot ub, lanes 32-63 slot ub + 1
       const int half = lane >> 5, jl = lane & 31;
       const uint64_t below_half = jl == 0 ? 0ull : (~0ull >> (64 - jl)) << (32 * half);
-      for (int ub = 2 * wave; ub < ns; ub += 2 * kSelWaves) {
+      for (int ub = 2 * wave; ub < ns; ub += 2 * WAVES) {
         const int u = ub + half;
         const int rr = R == 1 ? 0 : u / nt, t = u - rr * nt;
         const bool on = u < ns && jl < n_bpf && rank_of(bkey_s[rr * S + t][jl], bkey_s[rr * S + t], n_bpf) < kb;
@@ -170,7 +171,7 @@ __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D>
         if (on) out(rr)[(t0 + t) * kb + __popcll(m & below_half)] = frame(rr, t0 + t) * n_bpf + jl;
       }
     } else {
-      for (int u = wave; u < ns; u += kSelWaves) {
+      for (int u = wave; u < ns; u += WAVES) {
         const int rr = R == 1 ? 0 : u / nt, t = u - rr * nt;
         const bool on = lane < n_bpf && rank_of(bkey_s[rr * S + t][lane], bkey_s[rr * S + t], n_bpf) < kb;
         const uint64_t m = __ballot(on);
@@ -308,7 +309,9 @@ __host__ __device__ inline LongLds long_lds(int R, int n_mem, int n_kframes, int
 //   frames of M, so each frame mean an 8-lane group loads is dotted with both rows' q~
 //   slices (the same group inner product, term for term, as the listed kernel's), which
 //   halves the frame means' L2 traffic; each group keeps kLongUnroll frame means in
-//   flight. Scores are stored as 32-bit order-preserving bits per row.
+//   flight. Scores are stored as 32-bit order-preserving bits per row. Workgroups have
+//   512 threads, or 256 when |M| > 2048 (64 score registers per lane would otherwise
+//   leave too few workgroups per CU for one round).
 // - Wave w takes row w's top k_eff: the row's scores sit in registers (lane l holds
 //   positions l + 64 i of M), and each round takes the largest remaining score -- at its
 //   lowest position when several are equal, which ranks M as the listed kernel's
@@ -318,14 +321,18 @@ __host__ __device__ inline LongLds long_lds(int R, int n_mem, int n_kframes, int
 //   stages share passes (block_stage with two rows).
 constexpr int kLongUnroll = 4;                     // frame means in flight per group
 constexpr int kLongRows = 2;                       // rows per workgroup
+constexpr int kLongSlots = 16;                     // block-stage frames per pass
 constexpr int kLongBlockUnroll = 2;                // block means in flight per group
+// Threads per workgroup: 512 while the scores take at most 32 registers per lane (the
+// rows' workgroups then still fit the CUs in one round), else 256.
+constexpr int long_threads(int np) { return np <= 32 ? 512 : 256; }
 
 template <int D, int NP, bool BLOCKS>
-__global__ void __launch_bounds__(kSelThreads) select_long_kernel(SelectArgs a) {
-  constexpr int R = kLongRows;
-  static_assert(R >= 1 && R <= kSelWaves, "one row per wave in the top-k rounds");
+__global__ void __launch_bounds__(long_threads(NP)) select_long_kernel(SelectArgs a) {
+  constexpr int R = kLongRows, T = long_threads(NP), GROUPS = T / kGroup;
+  static_assert(R >= 1 && R <= T / kWave, "one row per wave in the top-k rounds");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_s[];
-  __shared__ uint64_t bkey_s[kSlots][64];
+  __shared__ uint64_t bkey_s[kLongSlots][64];
   const int n_mem = a.n_mem, W_f = a.W_f;
   const bool keep_all = a.k_eff >= n_mem;
   const LongLds L = long_lds(R, n_mem, a.n_kframes, W_f, keep_all);
@@ -352,7 +359,7 @@ __global__ void __launch_bounds__(kSelThreads) select_long_kernel(SelectArgs a) 
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) q[rr].v[i] = *reinterpret_cast<const float4*>(qr + 4 * c + 32 * i);
   }
-  for (int i = threadIdx.x; i < R * W_f; i += kSelThreads) t_s[i] = 0;   // every T_r entry a valid id
+  for (int i = threadIdx.x; i < R * W_f; i += T) t_s[i] = 0;   // every T_r entry a valid id
   if (wave == 0) {
     const uint64_t mw = lane < L.n_words ? a.masks.mem[lane] : 0ull;
     const uint64_t fw = lane < L.n_words ? a.masks.forced[lane] : 0ull;
@@ -367,17 +374,17 @@ __global__ void __launch_bounds__(kSelThreads) select_long_kernel(SelectArgs a) 
   if (!keep_all) {
     // kLongUnroll frame means per group in flight: each group walks ~|M| / 32 frames
     const float* kf = a.k_frm + static_cast<size_t>(bh) * a.kf_stride * D;
-    for (int e0 = grp; e0 < n_mem; e0 += kLongUnroll * kGroups) {
+    for (int e0 = grp; e0 < n_mem; e0 += kLongUnroll * GROUPS) {
       float4 k[kLongUnroll][D / 32];
 #pragma unroll
       for (int u = 0; u < kLongUnroll; ++u) {
-        const float* kr = kf + static_cast<size_t>(mem_s[min(e0 + u * kGroups, n_mem - 1)]) * D;
+        const float* kr = kf + static_cast<size_t>(mem_s[min(e0 + u * GROUPS, n_mem - 1)]) * D;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) k[u][i] = *reinterpret_cast<const float4*>(kr + 4 * c + 32 * i);
       }
 #pragma unroll
       for (int u = 0; u < kLongUnroll; ++u) {
-        const int e = e0 + u * kGroups;
+        const int e = e0 + u * GROUPS;
         if (e >= n_mem) break;
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
@@ -438,10 +445,10 @@ __global__ void __launch_bounds__(kSelThreads) select_long_kernel(SelectArgs a) 
   }
   if (!BLOCKS) return;
   __syncthreads();
-  block_stage<D, R, true, kLongBlockUnroll>(a, q, row0, nr, bh, W_f, t_s, bkey_s);
+  block_stage<D, R, true, kLongBlockUnroll, T, kLongSlots>(a, q, row0, nr, bh, W_f, t_s, bkey_s);
 }
 
-constexpr size_t kLongLdsMax = 160 * 1024 - sizeof(uint64_t) * kSlots * 64;
+constexpr size_t kLongLdsMax = 160 * 1024 - sizeof(uint64_t) * kLongSlots * 64;
 
 template <int D, int NP, bool BLOCKS>
 static hipError_t launch_select_long_np(const SelectArgs& a, int n_rows, hipStream_t st) {
@@ -457,7 +464,7 @@ static hipError_t launch_select_long_np(const SelectArgs& a, int n_rows, hipStre
     (void)hipGetLastError();
   }
   hipLaunchKernelGGL((select_long_kernel<D, NP, BLOCKS>), dim3(static_cast<unsigned>(n_bh * groups)),
-                     dim3(kSelThreads), static_cast<unsigned>(lds), st, a);
+                     dim3(long_threads(NP)), static_cast<unsigned>(lds), st, a);
   return hipGetLastError();
 }
 
