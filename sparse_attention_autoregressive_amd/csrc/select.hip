@@ -273,27 +273,36 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
   return pick<MAX>(b[0], b[1]);
 }
 
-// Sum of x over the lanes below this one.
+// Position of the largest score over the wave's (score, position) pairs, ties to the
+// lower position (positions are distinct); every lane gets it. Ties across lanes are
+// rare, so a single holder is read directly.
+__device__ __forceinline__ uint32_t wave_top_pos(uint32_t score, uint32_t pos) {
+  const uint32_t top = wave_reduce<true>(score);
+  const uint64_t holders = __ballot(score == top);
+  return __popcll(holders) == 1
+             ? static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pos), __builtin_ctzll(holders)))
+             : wave_reduce<false>(score == top ? pos : 0xFFFFFFFFu);
+}
+
+// Sum of x over the lanes below this one, for 0 <= x < 128: bit b of the sum's terms is
+// counted with a ballot, so no value crosses lanes through LDS.
 __device__ __forceinline__ int wave_excl_sum(int x) {
-  const int lane = threadIdx.x % kWave;
-  int s = x;
+  const uint64_t below = lanes_below_mask();
+  int s = 0;
 #pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    const int y = __shfl_up(s, m, kWave);
-    if (lane >= m) s += y;
-  }
-  return s - x;
+  for (int b = 0; b < 7; ++b) s += __popcll(__ballot((x >> b) & 1) & below) << b;
+  return s;
 }
 
 // LDS layout of select_long_kernel, in bytes from the start of dynamic LDS.
 struct LongLds {
-  int n_words, sc_stride;                // mask words per row; score entries per row (even)
+  int n_words, sc_stride;                // mask words per row; score entries per row (4 k)
   size_t bits, t, mem, total;            // offsets of the row bits, T_r, the ids of M; size
 };
 __host__ __device__ inline LongLds long_lds(int R, int n_mem, int n_kframes, int W_f, bool keep_all) {
   LongLds L;
   L.n_words = (n_kframes + 63) / 64;
-  L.sc_stride = (n_mem + 1) & ~1;
+  L.sc_stride = (n_mem + 3) & ~3;
   L.bits = keep_all ? 0 : static_cast<size_t>(R) * L.sc_stride * 4;
   L.t = L.bits + static_cast<size_t>(R) * L.n_words * 8;
   L.mem = L.t + static_cast<size_t>(R) * W_f * 2;
@@ -302,37 +311,39 @@ __host__ __device__ inline LongLds long_lds(int R, int n_mem, int n_kframes, int
 }
 
 // Selection for calls with more than kListFrames key frames (long histories).
-// - M and the always-kept frames arrive as bit masks; wave 0 takes one 64-frame word per
-//   lane and expands M into LDS in ascending order (a prefix count of the words'
-//   populations gives each lane its first position).
-// - A workgroup takes kLongRows consecutive rows of one head. Every row scores the same
-//   frames of M, so each frame mean an 8-lane group loads is dotted with both rows' q~
-//   slices (the same group inner product, term for term, as the listed kernel's), which
-//   halves the frame means' L2 traffic; each group keeps kLongUnroll frame means in
-//   flight. Scores are stored as 32-bit order-preserving bits per row. Workgroups have
-//   512 threads, or 256 when |M| > 2048 (64 score registers per lane would otherwise
-//   leave too few workgroups per CU for one round).
-// - Wave w takes row w's top k_eff: the row's scores sit in registers (lane l holds
-//   positions l + 64 i of M), and each round takes the largest remaining score -- at its
-//   lowest position when several are equal, which ranks M as the listed kernel's
-//   (score, lower frame id first) keys do, since positions ascend with frame ids -- sets
-//   the frame's bit over the always-kept frames' bits and clears the score.
+// - M and the always-kept frames arrive as bit masks. Wave 0 stores M's 64-frame words
+//   and, per word, the count of members before it (a prefix over the words'
+//   populations); every thread then places its frames' ids in ascending order.
+// - A 512-thread workgroup takes kLongRows consecutive rows of one head. Every row scores
+//   the same frames of M, so each frame mean an 8-lane group loads is dotted with both
+//   rows' q~ slices (the same group inner product, term for term, as the listed
+//   kernel's), which halves the frame means' L2 traffic; each group keeps kLongUnroll
+//   frame means in flight. Scores are stored as 32-bit order-preserving bits per row.
+// - Wave w takes row w's top k_eff (lane l reads positions 4 l + 256 i + 0..3 of M,
+//   16 bytes at a time). The largest score wins, at its lowest position when several are
+//   equal, which ranks M as the listed kernel's (score, lower frame id first) keys do,
+//   since positions ascend with frame ids. The candidates are first cut to the scores at
+//   or above the k_eff-th largest of the lanes' maxima (they include the top k_eff); up to
+//   64 of them, one per lane, leave each round two wave reductions. Otherwise (k_eff > 64,
+//   or many equal scores) each round scans all of the row's scores. Each winner sets its
+//   frame's bit over the always-kept frames' bits.
 // - Each row's bits are compacted into T_r by the same prefix count, and both rows' block
 //   stages share passes (block_stage with two rows).
 constexpr int kLongUnroll = 4;                     // frame means in flight per group
 constexpr int kLongRows = 2;                       // rows per workgroup
 constexpr int kLongSlots = 16;                     // block-stage frames per pass
 constexpr int kLongBlockUnroll = 2;                // block means in flight per group
-// Threads per workgroup: 512 while the scores take at most 32 registers per lane (the
-// rows' workgroups then still fit the CUs in one round), else 256.
-constexpr int long_threads(int np) { return np <= 32 ? 512 : 256; }
+constexpr int kLongThreads = 512;                  // threads per workgroup
 
-template <int D, int NP, bool BLOCKS>
-__global__ void __launch_bounds__(long_threads(NP)) select_long_kernel(SelectArgs a) {
-  constexpr int R = kLongRows, T = long_threads(NP), GROUPS = T / kGroup;
+template <int D, bool BLOCKS>
+__global__ void __launch_bounds__(kLongThreads) select_long_kernel(SelectArgs a) {
+  constexpr int R = kLongRows, T = kLongThreads, GROUPS = T / kGroup;
   static_assert(R >= 1 && R <= T / kWave, "one row per wave in the top-k rounds");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_s[];
   __shared__ uint64_t bkey_s[kLongSlots][64];
+  __shared__ uint64_t mw_s[kMaxFrames / 64];       // M's mask words
+  __shared__ int16_t pre_s[kMaxFrames / 64];       // members of M in the words before
+  __shared__ uint2 cand_s[kLongRows][kWave];       // top-k candidates (score, position) per row
   const int n_mem = a.n_mem, W_f = a.W_f;
   const bool keep_all = a.k_eff >= n_mem;
   const LongLds L = long_lds(R, n_mem, a.n_kframes, W_f, keep_all);
@@ -360,15 +371,25 @@ __global__ void __launch_bounds__(long_threads(NP)) select_long_kernel(SelectArg
     for (int i = 0; i < D / 32; ++i) q[rr].v[i] = *reinterpret_cast<const float4*>(qr + 4 * c + 32 * i);
   }
   for (int i = threadIdx.x; i < R * W_f; i += T) t_s[i] = 0;   // every T_r entry a valid id
+  if (!keep_all && threadIdx.x < R * (L.sc_stride - n_mem))      // score places past |M|: none
+    sc_s[(threadIdx.x / (L.sc_stride - n_mem)) * L.sc_stride + n_mem + threadIdx.x % (L.sc_stride - n_mem)] = 0u;
+  static_assert(kMaxFrames / 64 == kWave, "one mask word per lane of wave 0");
   if (wave == 0) {
     const uint64_t mw = lane < L.n_words ? a.masks.mem[lane] : 0ull;
     const uint64_t fw = lane < L.n_words ? a.masks.forced[lane] : 0ull;
-    int pos = wave_excl_sum(__popcll(mw));
-    for (uint64_t m = mw; m; m &= m - 1) mem_s[pos++] = static_cast<int16_t>(64 * lane + __builtin_ctzll(m));
+    mw_s[lane] = mw;
+    pre_s[lane] = static_cast<int16_t>(wave_excl_sum(__popcll(mw)));
     if (lane < L.n_words) {
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) bits_s[rr * L.n_words + lane] = keep_all ? (fw | mw) : fw;
     }
+  }
+  __syncthreads();
+  // M's ids in ascending order: frame f goes to the members below it
+  for (int f = threadIdx.x; f < a.n_kframes; f += T) {
+    const uint64_t w = mw_s[f / 64];
+    const int b = f % 64;
+    if ((w >> b) & 1ull) mem_s[pre_s[f / 64] + __popcll(w & ((1ull << b) - 1))] = static_cast<int16_t>(f);
   }
   __syncthreads();
   if (!keep_all) {
@@ -397,36 +418,83 @@ __global__ void __launch_bounds__(long_threads(NP)) select_long_kernel(SelectArg
     }
     __syncthreads();
     if (wave < nr) {
-      // the row's scores in registers, element i of a lane at position lane + 64 i of M
-      // (NP * 64 >= |M|; empty places hold 0, below every score). A round takes the
-      // largest remaining score, at its lowest position when several lanes hold it, and
-      // clears it.
-      const uint32_t* scr = sc_s + wave * L.sc_stride;
-      uint32_t sc[NP];
+      // wave w: row w's scores in LDS; lane l reads positions 4 l + 256 i + (0..3) of M
+      // (consecutive lanes, consecutive 16-byte chunks: no bank conflicts), four chunks
+      // per batch
+      uint32_t* scr = sc_s + wave * L.sc_stride;
+      uint64_t* bits = bits_s + wave * L.n_words;
+      auto scan = [&](auto&& f) {                // f(score, position), ascending positions
+        for (int b0 = 4 * lane; b0 < n_mem; b0 += 4 * 4 * kWave) {
+          uint4 v[4];
 #pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        const int e = lane + kWave * i;
-        sc[i] = e < n_mem ? scr[e] : 0u;
-      }
-      for (int r = 0; r < a.k_eff; ++r) {
-        uint32_t best = 0;
-        int bi = 0;
+          for (int u = 0; u < 4; ++u) {
+            const int p = b0 + u * 4 * kWave;
+            v[u] = p < n_mem ? *reinterpret_cast<const uint4*>(scr + p) : make_uint4(0, 0, 0, 0);
+          }
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const bool gt = sc[i] > best;
-          best = gt ? sc[i] : best;
-          bi = gt ? i : bi;
+          for (int u = 0; u < 4; ++u) {
+            const int p = b0 + u * 4 * kWave;
+            if (p < n_mem) {                     // places past |M| in the chunk hold 0
+              f(v[u].x, p);
+              f(v[u].y, p + 1);
+              f(v[u].z, p + 2);
+              f(v[u].w, p + 3);
+            }
+          }
         }
-        const uint32_t top = wave_reduce<true>(best);
-        const int win = min(static_cast<int>(wave_reduce<false>(best == top ? static_cast<uint32_t>(lane + kWave * bi)
-                                                                            : 0xFFFFFFFFu)),
-                            n_mem - 1);
-        const int dw = win - lane;
-#pragma unroll
-        for (int i = 0; i < NP; ++i) sc[i] = dw == kWave * i ? 0u : sc[i];
+      };
+      auto keep = [&](uint32_t pos) {
         if (lane == 0) {
-          const int f = mem_s[win];
-          bits_s[wave * L.n_words + f / 64] |= 1ull << (f % 64);
+          const int f = mem_s[min(static_cast<int>(pos), n_mem - 1)];
+          bits[f / 64] |= 1ull << (f % 64);
+        }
+      };
+      // Candidates: every score at or above t, the k_eff-th largest of the lanes' maxima.
+      // The lanes holding those maxima hold k_eff scores >= t, so the row's top k_eff are
+      // all candidates; with at most 64 of them, one per lane, a round is two reductions.
+      bool done = false;
+      if (a.k_eff <= kWave) {
+        uint32_t v = 0;
+        scan([&](uint32_t x, int) { v = max(v, x); });
+        uint32_t t = 0;
+        for (int r = 0; r < a.k_eff; ++r) {
+          t = wave_reduce<true>(v);
+          if (lane == __builtin_ctzll(__ballot(v == t))) v = 0;
+        }
+        t = max(t, 1u);                          // 0 is no score
+        int cnt = 0;
+        scan([&](uint32_t x, int) { cnt += x >= t ? 1 : 0; });
+        int off = wave_excl_sum(cnt);            // cnt <= 4 |M| / 256 <= 64
+        const int total = __builtin_amdgcn_readlane(off + cnt, kWave - 1);
+        if (total <= kWave) {
+          uint2* cand = cand_s[wave];
+          scan([&](uint32_t x, int p) {
+            if (x >= t) cand[off++] = make_uint2(x, static_cast<uint32_t>(p));
+          });
+          uint32_t cs = lane < total ? cand[lane].x : 0u;
+          const uint32_t cp = lane < total ? cand[lane].y : 0u;
+          for (int r = 0; r < a.k_eff; ++r) {
+            const uint32_t win = wave_top_pos(cs, cp);
+            if (cp == win) cs = 0u;
+            keep(win);
+          }
+          done = true;
+        }
+      }
+      if (!done) {
+        // every score: a round takes the largest remaining and clears it (lane 0 writes
+        // the 0; the wave's later reads of the row see it, LDS operations of a wave
+        // being done in order)
+        for (int r = 0; r < a.k_eff; ++r) {
+          uint32_t best = 0, bpos = 0;
+          scan([&](uint32_t x, int p) {
+            const bool gt = x > best;            // ascending positions: ties keep the lower
+            best = gt ? x : best;
+            bpos = gt ? static_cast<uint32_t>(p) : bpos;
+          });
+          const uint32_t win = wave_top_pos(best, bpos);
+          if (lane == 0) scr[min(static_cast<int>(win), n_mem - 1)] = 0u;
+          keep(win);
         }
       }
     }
@@ -450,8 +518,8 @@ __global__ void __launch_bounds__(long_threads(NP)) select_long_kernel(SelectArg
 
 constexpr size_t kLongLdsMax = 160 * 1024 - sizeof(uint64_t) * kLongSlots * 64;
 
-template <int D, int NP, bool BLOCKS>
-static hipError_t launch_select_long_np(const SelectArgs& a, int n_rows, hipStream_t st) {
+template <int D, bool BLOCKS>
+static hipError_t launch_select_long_d(const SelectArgs& a, int n_rows, hipStream_t st) {
   const int n_bh = n_rows / a.n_qb, groups = (a.n_qb + kLongRows - 1) / kLongRows;
   const size_t lds = long_lds(kLongRows, a.n_mem, a.n_kframes, a.W_f, a.k_eff >= a.n_mem).total;
   if (lds > kLongLdsMax) return hipErrorInvalidValue;
@@ -459,23 +527,13 @@ static hipError_t launch_select_long_np(const SelectArgs& a, int n_rows, hipStre
     // dynamic LDS past 64 KB is declared for the kernel (up to the 160 KB a workgroup can
     // address); a runtime that does not need the declaration may refuse it, so its status
     // is cleared and the launch's own status decides
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&select_long_kernel<D, NP, BLOCKS>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&select_long_kernel<D, BLOCKS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLongLdsMax));
     (void)hipGetLastError();
   }
-  hipLaunchKernelGGL((select_long_kernel<D, NP, BLOCKS>), dim3(static_cast<unsigned>(n_bh * groups)),
-                     dim3(long_threads(NP)), static_cast<unsigned>(lds), st, a);
+  hipLaunchKernelGGL((select_long_kernel<D, BLOCKS>), dim3(static_cast<unsigned>(n_bh * groups)),
+                     dim3(kLongThreads), static_cast<unsigned>(lds), st, a);
   return hipGetLastError();
-}
-
-// Scores per lane in the top-k rounds: the smallest of 8, 16, 32, 64 that covers M.
-template <int D, bool BLOCKS>
-static hipError_t launch_select_long_d(const SelectArgs& a, int n_rows, hipStream_t st) {
-  static_assert(kMaxFrames <= 64 * kWave, "64 scores per lane cover every memory set");
-  if (a.n_mem <= 8 * kWave) return launch_select_long_np<D, 8, BLOCKS>(a, n_rows, st);
-  if (a.n_mem <= 16 * kWave) return launch_select_long_np<D, 16, BLOCKS>(a, n_rows, st);
-  if (a.n_mem <= 32 * kWave) return launch_select_long_np<D, 32, BLOCKS>(a, n_rows, st);
-  return launch_select_long_np<D, 64, BLOCKS>(a, n_rows, st);
 }
 
 template <int D, bool FRAMES, bool BLOCKS>

@@ -86,3 +86,19 @@ def test_long_history_separate_calls_equal_fused():
     assert np.array_equal(frames.cpu().numpy(), gpu["frames"])
     assert np.array_equal(blocks.cpu().numpy(), gpu["blocks"])
     assert np.array_equal(blocks2.cpu().numpy(), gpu["blocks"])
+
+
+def test_long_history_equal_scores_take_lowest_ids():
+    # zero queries: every frame score is exactly 0, so each row's top k_f of M are its
+    # k_f lowest frame ids (the pages' ranking with ties to the lower id), and each
+    # frame's top k_b blocks its k_b lowest block indices
+    w = _long(700, H=1, d=64, dtype="fp32", k_f=20, k_b=1, name="long_history_ties")
+    x = synth.make(w)
+    x = replace(x, q=torch.zeros_like(x.q))
+    gpu = run_gpu(w, x, w.k_b)
+    want = sorted(set(w.forced) | set(sorted(w.mem)[:w.k_f]))
+    frames = gpu["frames"].reshape(-1, gpu["frames"].shape[-1])
+    assert all(list(f) == want for f in frames)
+    blocks = gpu["blocks"].reshape(-1, gpu["blocks"].shape[-1])
+    nb = lf.n_bpf(lf.Geom(w.B, w.H, w.d, w.tpf, w.bs))
+    assert all(list(b) == [f * nb for f in want] for b in blocks)
