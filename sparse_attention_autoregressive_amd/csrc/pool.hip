@@ -391,15 +391,6 @@ __device__ __forceinline__ void prologue_block(const ProJob<T>& p, int w, int tp
           ++row;
         }
       }
-      const int pos[3] = {pos_t, row, col};
-      float rc[E / 2], rs[E / 2];
-#pragma unroll
-      for (int m = 0; m < E / 2; ++m) {
-        float r = static_cast<float>(pos[axis[m]]) * rev[m];
-        r -= rintf(r);
-        rc[m] = __builtin_amdgcn_cosf(r);
-        rs[m] = __builtin_amdgcn_sinf(r);
-      }
       float x[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
@@ -409,17 +400,20 @@ __device__ __forceinline__ void prologue_block(const ProJob<T>& p, int w, int tp
       for (int e = 0; e < E; ++e) ss = fmaf(x[e], x[e], ss);
       ss = token_sum<C>(ss);
       const float inv = rsqrtf(ss * (1.0f / D) + p.eps);
-      float o[E];
+      // each pair rotated as soon as its angle is known, in place (few live registers)
 #pragma unroll
       for (int m = 0; m < E / 2; ++m) {
+        float r = static_cast<float>(axis[m] == 0 ? pos_t : (axis[m] == 1 ? row : col)) * rev[m];
+        r -= rintf(r);
+        const float rc = __builtin_amdgcn_cosf(r), rs = __builtin_amdgcn_sinf(r);
         const float y0 = x[2 * m] * inv * gm[2 * m], y1 = x[2 * m + 1] * inv * gm[2 * m + 1];
-        o[2 * m] = Out16<T>::round(y0 * rc[m] - y1 * rs[m]);
-        o[2 * m + 1] = Out16<T>::round(y0 * rs[m] + y1 * rc[m]);
+        x[2 * m] = Out16<T>::round(y0 * rc - y1 * rs);
+        x[2 * m + 1] = Out16<T>::round(y0 * rs + y1 * rc);
       }
       const bool valid = t < len;
-      if (valid) Out16<T>::store(yout + static_cast<size_t>(t) * D, o);
+      if (valid) Out16<T>::store(yout + static_cast<size_t>(t) * D, x);
 #pragma unroll
-      for (int e = 0; e < E; ++e) A[e] += valid ? o[e] : 0.f;
+      for (int e = 0; e < E; ++e) A[e] += valid ? x[e] : 0.f;
     }
   }
   // the block mean from the four quarter sums, in the order lf_pool uses
