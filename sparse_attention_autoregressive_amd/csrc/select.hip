@@ -1,5 +1,6 @@
 // Two-level mask selection (Light Forcing summary, execution flow, stage 3; technical
-// summary section 2.2), one 256-thread workgroup per row (b, h, query block r).
+// summary section 2.2), one 256-thread workgroup per row (b, h, query block r) for up to
+// kListFrames key frames; longer histories take select_long_kernel (further below).
 //
 // Scores. Every inner product of the row's pooled query q~_r with a pooled key (a frame
 // mean k^_f or a block mean k~_j^(tau)) is computed by a group of 8 lanes: lane c of the
@@ -101,10 +102,11 @@ __device__ __forceinline__ int frame_at(const TS* t_s, const SelectArgs& a, int 
   return FRAMES ? t_s[t] : min(max(a.frames_in[static_cast<size_t>(row) * W_f + t], 0), a.n_kframes - 1);
 }
 
-// Block stage of nr <= R rows of one head: each row's T_r (t_s + rr * W_f, or the
-// caller's list), kSlots / R frames of every row per pass, each frame's n_bpf block
-// scores ranked and the chosen ids written ascending. Group g scores the blocks of row
-// g % R with that row's q~ slices, so the R rows share each pass and its barriers.
+// Block stage of nr <= R rows of one head on T threads: each row's T_r (t_s + rr * W_f,
+// or the caller's list), SLOTS / R frames of every row per pass, each frame's n_bpf
+// block scores ranked and the chosen ids written ascending. Group g scores the blocks of
+// row g % R with that row's q~ slices, U block means in flight, so the R rows share each
+// pass and its barriers.
 template <int D, int R, bool FRAMES, int U = 1, int T = kSelThreads, int SLOTS = kSlots, typename TS>
 __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D> (&q)[R], int row0, int nr, int bh,
                                             int W_f, const TS* t_s, uint64_t (*bkey_s)[64]) {
@@ -136,7 +138,6 @@ __device__ __forceinline__ void block_stage(const SelectArgs& a, const QSlice<D>
   for (int t0 = 0; t0 < W_f; t0 += S) {
     const int nt = min(S, W_f - t0);
     if (gr < nr) {
-      // U block means per group in flight
       const int ne = nt * n_bpf;
       for (int e0 = gi; e0 < ne; e0 += U * GR) {
         float4 k[U][D / 32];
