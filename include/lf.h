@@ -237,7 +237,8 @@ lf_status lf_qk_prologue_step(const void* q, const void* k_new, void* q_out, voi
  * Limits: d in {64, 128}; n_kframes <= 4096 (about 16 minutes of 480p latent frames);
  *   k_f >= 0. Up to 256 key frames the frame stage ranks by counting (one frame of M per
  *   thread); beyond, two rows of a head share each workgroup and each row takes its k_f
- *   best in k_f rounds of a wave-wide maximum, with the same result.
+ *   best in k_f rounds of a wave-wide maximum (over the scores at or above the k_f-th
+ *   largest lane maximum when at most 64 are), with the same result.
  * Errors: LF_ERR_INVALID_ARG, LF_ERR_UNSUPPORTED (d, n_kframes), LF_ERR_HIP.
  * ------------------------------------------------------------------------------- */
 lf_status lf_select_frames(const float* q_blk, const float* k_frm, lf_geom g, int32_t n_qb,
