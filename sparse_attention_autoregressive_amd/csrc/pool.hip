@@ -70,6 +70,8 @@ __device__ __forceinline__ float token_lane_sum(float x) {
 constexpr int kBatch = 16;
 constexpr int kQuarters = 4;
 constexpr int kQuarter = kBatch / kQuarters;
+constexpr int kProLoads = 2;         // prologue loads in flight per lane (kQuarter a multiple)
+static_assert(kQuarter % kProLoads == 0, "whole steps per quarter");
 
 template <int E, int C>
 __device__ __forceinline__ void combine_quarters(const float (&A)[kQuarters][E], float* sum) {
@@ -369,20 +371,26 @@ __device__ __forceinline__ void prologue_block(const ProJob<T>& p, int w, int tp
 #pragma unroll
   for (int e = 0; e < E; ++e) A[e] = 0.f;
   for (int t0 = 0; t0 < len; t0 += kBatch * TL) {
-    uint4 v[kQuarter];
-#pragma unroll
-    for (int u = 0; u < kQuarter; ++u) {
-      const int t = t0 + s + (q * kQuarter + u) * TL;
-      v[u] = t < len ? *reinterpret_cast<const uint4*>(xin + static_cast<size_t>(t) * D) : make_uint4(0, 0, 0, 0);
-    }
     // the lane's first token of this quarter: row and column by one division, then the
     // column advances by TL per token (wrapping into the next row; a row narrower than TL
     // wraps several times)
     const int tok = j * bs + t0 + s + q * kQuarter * TL;
     int row = tok / p.lat_w;
     int col = tok - row * p.lat_w;
+    // the quarter's loads kProLoads at a time, in a loop the compiler keeps rolled: the
+    // kernel then fits 64 VGPRs and eight waves per SIMD; the tokens are transformed and
+    // added in the same order as with the whole quarter in flight
+#pragma unroll 1
+    for (int h = 0; h < kQuarter; h += kProLoads) {
+      uint4 v[kProLoads];
 #pragma unroll
-    for (int u = 0; u < kQuarter; ++u) {
+      for (int i = 0; i < kProLoads; ++i) {
+        const int t = t0 + s + (q * kQuarter + h + i) * TL;
+        v[i] = t < len ? *reinterpret_cast<const uint4*>(xin + static_cast<size_t>(t) * D) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int i = 0; i < kProLoads; ++i) {
+      const int u = h + i;
       const int t = t0 + s + (q * kQuarter + u) * TL;
       if (u > 0) {
         col += TL;
@@ -394,7 +402,7 @@ __device__ __forceinline__ void prologue_block(const ProJob<T>& p, int w, int tp
       float x[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
-      Chunk16<T>::add(reinterpret_cast<const T*>(&v[u]), x);
+      Chunk16<T>::add(reinterpret_cast<const T*>(&v[i]), x);
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) ss = fmaf(x[e], x[e], ss);
@@ -414,6 +422,7 @@ __device__ __forceinline__ void prologue_block(const ProJob<T>& p, int w, int tp
       if (valid) Out16<T>::store(yout + static_cast<size_t>(t) * D, x);
 #pragma unroll
       for (int e = 0; e < E; ++e) A[e] += valid ? x[e] : 0.f;
+    }
     }
   }
   // the block mean from the four quarter sums, in the order lf_pool uses
