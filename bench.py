@@ -324,7 +324,7 @@ def main():
                     help="first run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build targets one GPU; the HSA path has no multi-GPU mode "
+        print("bench.py: the HSA path runs on one GPU and has no multi-GPU mode "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -852,8 +852,8 @@ def compare_schedules(args, s, g, sp_cag, sw_cag, layers, o):
     """CAG against the uniform allocation under the same FLOP budget, and both against
     dense attention: wall time per sweep (all layers) and, on two layers, each chunk's
     relative L2 distance of the attention output from the dense output (a per-chunk
-    fidelity measure on synthetic inputs; the pages judge the schedules by the quality of
-    generated video, which needs a trained model)."""
+    fidelity measure on synthetic inputs; the pages compare the schedules by the quality
+    of generated video, which needs a trained model)."""
     dev = o.device
     sp_uni = plan_sweep(g, s.n_chunks, s.frames_per_chunk, s.k_f, s.T, s.s_base, s.s_target, s.d ** -0.5,
                         schedule="uniform")
