@@ -394,7 +394,7 @@ __global__ void __launch_bounds__(kLongThreads) select_long_kernel(SelectArgs a)
   }
   __syncthreads();
   if (!keep_all) {
-    // kLongUnroll frame means per group in flight: each group walks ~|M| / 32 frames
+    // kLongUnroll frame means per group in flight: each group walks ~|M| / 64 frames
     const float* kf = a.k_frm + static_cast<size_t>(bh) * a.kf_stride * D;
     for (int e0 = grp; e0 < n_mem; e0 += kLongUnroll * GROUPS) {
       float4 k[kLongUnroll][D / 32];
