@@ -53,6 +53,12 @@ def test_long_history_masks_and_attention(n, tpf):
     assert hit > 1.0, hit
 
 
+def test_long_history_480p_block_geometry():
+    # 300 key frames at the 480p frame and block sizes (1560 tokens, 25 blocks per frame
+    # with a 24-token tail, 75 query blocks), one head, k_f = 4 and k_b = 8 as at chunk 7
+    _check(_long(300, H=1, d=128, tpf=1560, bs=64, k_f=4, k_b=8, name="long_history_480p"))
+
+
 def test_long_history_max_frames_fp32():
     # the 4096-frame limit: 4092 memory frames, the dynamic LDS at its largest
     _check(_long(4096, H=1, d=64, dtype="fp32", k_f=8, name="long_history_4096_fp32"))
