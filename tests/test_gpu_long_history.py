@@ -59,6 +59,11 @@ def test_long_history_480p_block_geometry():
     _check(_long(300, H=1, d=128, tpf=1560, bs=64, k_f=4, k_b=8, name="long_history_480p"))
 
 
+def test_long_history_two_batches():
+    # B = 2: the (b, h) slices of q~, k^ and k~ and the rows' workgroups across the batch
+    _check(_long(300, B=2, H=2, d=64, dtype="fp32", k_f=5, name="long_history_batch2"))
+
+
 def test_long_history_max_frames_fp32():
     # the 4096-frame limit: 4092 memory frames, the dynamic LDS at its largest
     _check(_long(4096, H=1, d=64, dtype="fp32", k_f=8, name="long_history_4096_fp32"))
